@@ -1,0 +1,268 @@
+"""Benchmark of the fused small-channel convolution + epilogue kernels on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--ops all|none]
+                    [--no-cpu-baseline] [--seed S]
+
+One step is one call of the headline workload's fused operator on one batch
+of seeded synthetic input already resident in device memory (the default
+headline is Conv2d 3x3 8->64 + ReLU + HardSwish at N = 128, 128 x 128).
+W untimed warm-up steps, then exactly K timed steps bracketed by device
+synchronisations; HIP events on the stream the kernels run on give the
+per-launch kernel time.  Rank 0 prints one JSON line with the headline
+throughput (GFLOP/s of the convolution's multiply-adds, 2 FLOP each), the
+roofline of the dominant kernel, the CPU oracle's throughput on a bounded
+sample (a baseline, not a target) and, under "ops", the same measurement for
+every fused workload.
+
+Only one GPU exists per box and nothing here is distributed: --gpus above 1
+exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+from conv_inputs import CONV2D, CONV3D, CONVT, WORKLOADS, workload_inputs  # noqa: E402
+
+METRIC = "fused conv+epilogue ms per call, GFLOP/s & % of fp32/HBM roofline (1 MI355X)"
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
+HEADLINE = "conv2d_relu_hswish_n128"
+
+KERNEL_SOURCES = {
+    CONV2D: "conv2d_relu_hswish.hip",
+    CONV3D: "conv3d_lrelu_add_clamp_gelu.hip",
+    CONVT: "convT2d_pool_htanh_mean_tanh.hip",
+}
+
+
+def work_counts(shape: dict) -> dict:
+    """Algorithmic work of one call: multiply-adds of the convolution (epilogue
+    excluded) and bytes that must cross HBM (read x, w, b, s once; write y once)."""
+    op, N, Ci, Co, k = shape["op"], shape["N"], shape["C_in"], shape["C_out"], shape["k"]
+    if op == CONV2D:
+        Ho, Wo = shape["H"] - k + 1, shape["W"] - k + 1
+        outs = N * Co * Ho * Wo
+        fma = outs * Ci * k * k
+        nbytes = 4 * (N * Ci * shape["H"] * shape["W"] + Co * Ci * k * k + Co + outs)
+    elif op == CONV3D:
+        Do, Ho, Wo = shape["D"] - k + 1, shape["H"] - k + 1, shape["W"] - k + 1
+        outs = N * Co * Do * Ho * Wo
+        fma = outs * Ci * k ** 3
+        nbytes = 4 * (N * Ci * shape["D"] * shape["H"] * shape["W"] + Co * Ci * k ** 3 + 2 * Co + outs)
+    else:
+        Ho, Wo = shape["H"], shape["W"]  # stride 1, padding 1, k = 3
+        conv_outs = N * Co * Ho * Wo
+        fma = conv_outs * Ci * k * k
+        nbytes = 4 * (N * Ci * shape["H"] * shape["W"] + Ci * Co * k * k + Co + N * Co)
+    return {"fma": fma, "flop": 2 * fma, "bytes": nbytes}
+
+
+def source_digest(op: str) -> str:
+    src = ROOT / "channel_convolution_epilogue_amd" / "csrc" / KERNEL_SOURCES[op]
+    return hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+
+
+def measured_traffic(op: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counts, used only while the kernel source still matches the profiled one."""
+    f = ROOT / "profiles" / "hbm_traffic.json"
+    if not f.exists():
+        return None
+    try:
+        rec = json.loads(f.read_text()).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_digest(op):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run_op(cce, shape, d):
+    op = shape["op"]
+    if op == CONV2D:
+        return lambda: cce.conv2d_relu_hswish(d["x"], d["w"], d["b"], out=d["y"])
+    if op == CONV3D:
+        return lambda: cce.conv3d_lrelu_add_clamp_gelu(d["x"], d["w"], d["b"], d["s"], shape["slope"],
+                                                       shape["lo"], shape["hi"], out=d["y"])
+    return lambda: cce.convT2d_pool_htanh_mean_tanh(d["x"], d["w"], d["b"], out=d["y"],
+                                                    htanh_lo=shape["lo"], htanh_hi=shape["hi"],
+                                                    workspace=d["ws"])
+
+
+def device_inputs(torch, cce, shape, p):
+    d = {k: torch.from_numpy(v).cuda() for k, v in p.items()}
+    N, Co, k = shape["N"], shape["C_out"], shape["k"]
+    if shape["op"] == CONV2D:
+        d["y"] = torch.empty((N, Co, shape["H"] - k + 1, shape["W"] - k + 1), device="cuda")
+    elif shape["op"] == CONV3D:
+        d["y"] = torch.empty((N, Co, shape["D"] - k + 1, shape["H"] - k + 1, shape["W"] - k + 1),
+                             device="cuda")
+    else:
+        d["y"] = torch.empty((N, Co, 1, 1), device="cuda")
+        nb = cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(N, shape["C_in"], shape["H"], shape["W"], Co)
+        d["ws"] = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    return d
+
+
+def time_workload(torch, cce, name, steps, warmup, seed):
+    shape, p = workload_inputs(name, seed)
+    d = device_inputs(torch, cce, shape, p)
+    del p
+    fn = run_op(cce, shape, d)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / steps  # one launch per step
+    wc = work_counts(shape)
+    out = {
+        "ms_per_call": kernel_ms,
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "gflops": wc["flop"] / (kernel_ms * 1e-3) / 1e9,
+        "gbs": wc["bytes"] / (kernel_ms * 1e-3) / 1e9,
+        "fma": wc["fma"],
+        "algorithmic_bytes": wc["bytes"],
+    }
+    tflops = wc["flop"] / (kernel_ms * 1e-3) / 1e12
+    out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+                       "traffic": measured_traffic(shape["op"], name)}
+    out["hbm_frac"] = round(out["gbs"] / PEAK_HBM_GBS, 4)
+    del d
+    torch.cuda.empty_cache()
+    return shape, out
+
+
+def cpu_baseline(name, seed, budget_s=12.0):
+    """The CPU oracle (double precision, OpenMP over all host cores) timed on a
+    bounded sample of the workload, scaled to GFLOP/s of the same algorithmic count."""
+    import oracle as O
+    shape, p = workload_inputs(name, seed)
+    op = shape["op"]
+    cores = O.num_threads()
+    rng = np.random.default_rng(seed)
+    if op in (CONV2D, CONV3D):
+        # whole images, as many as fit the time budget (at least one)
+        per_image = work_counts(dict(shape, N=1))["fma"]
+        t = time.perf_counter()
+        x1 = np.ascontiguousarray(p["x"][:1])
+        if op == CONV2D:
+            O.conv2d_relu_hswish(x1, p["w"], p["b"])
+        else:
+            O.conv3d_lrelu_add_clamp_gelu(x1, p["w"], p["b"], p["s"], shape["slope"], shape["lo"], shape["hi"])
+        one = time.perf_counter() - t
+        n = int(max(1, min(shape["N"], budget_s / max(one, 1e-6))))
+        xs = np.ascontiguousarray(p["x"][:n])
+        t = time.perf_counter()
+        if op == CONV2D:
+            O.conv2d_relu_hswish(xs, p["w"], p["b"])
+        else:
+            O.conv3d_lrelu_add_clamp_gelu(xs, p["w"], p["b"], p["s"], shape["slope"], shape["lo"], shape["hi"])
+        dt = time.perf_counter() - t
+        sample = f"{n} of {shape['N']} images, full output"
+        fma = per_image * n
+    else:
+        per_plane = work_counts(shape)["fma"] // (shape["N"] * shape["C_out"])
+        t = time.perf_counter()
+        O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], np.arange(cores))
+        one = (time.perf_counter() - t) / cores
+        count = int(max(cores, min(shape["N"] * shape["C_out"], budget_s / max(one, 1e-6))))
+        idx = rng.choice(shape["N"] * shape["C_out"], size=count, replace=False)
+        t = time.perf_counter()
+        O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], idx)
+        dt = time.perf_counter() - t
+        sample = f"{count} of {shape['N'] * shape['C_out']} (image, channel) outputs"
+        fma = per_plane * count
+    return {"value": round(2 * fma / dt / 1e9, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description="fused conv + epilogue benchmark (one MI355X)")
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--ops", default="all", choices=["all", "none"],
+                    help="also time every other fused workload (reported under 'ops')")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: every box here has one MI355X and the fused "
+              "kernels have no multi-GPU path (DESIGN.md describes how the batch would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    import channel_convolution_epilogue_amd as cce
+    cce.load()
+
+    shape, head = time_workload(torch, cce, args.workload, args.steps, args.warmup, args.seed)
+    print(f"# {args.workload}: {head['ms_per_call']:.4f} ms/call, {head['gflops']:.1f} GFLOP/s, "
+          f"{head['roofline']['frac']:.3f} of fp32 MFMA peak", file=sys.stderr, flush=True)
+    ops = {}
+    if args.ops == "all":
+        for name in WORKLOADS:
+            if name == args.workload:
+                r = head
+            else:
+                _, r = time_workload(torch, cce, name, max(3, min(args.steps, 20)), min(args.warmup, 3),
+                                     args.seed)
+                print(f"# {name}: {r['ms_per_call']:.4f} ms/call, {r['gflops']:.1f} GFLOP/s, "
+                      f"{r['roofline']['frac']:.3f} of fp32 MFMA peak", file=sys.stderr, flush=True)
+            ops[name] = {"ms_per_call": round(r["ms_per_call"], 5), "gflops": round(r["gflops"], 1),
+                         "gbs": round(r["gbs"], 1), "roofline_frac": r["roofline"]["frac"],
+                         "hbm_frac": r["hbm_frac"]}
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["gflops"], 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_call"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, **{k: v for k, v in shape.items() if k != "op"},
+                   "op": shape["op"], "global_batch": shape["N"], "parallelism": "none (1 GPU)"},
+        "roofline": head["roofline"],
+        "hbm": {"achieved": round(head["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": head["hbm_frac"]},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.seed)
+    if ops:
+        line["ops"] = ops
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+// extern "C" entry points of libcce: argument validation (host only, before any
+// HIP call), then one kernel launch per call.  No allocation, no
+// synchronisation and no mutable global state beyond a per-device cache of
+// device properties.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "cce.h"
+#include "cce_internal.hpp"
+
+namespace cce {
+
+namespace {
+constexpr int kMaxDevices = 64;
+// Cached per device: CU count and LDS bytes per workgroup (0 = not yet read).
+std::atomic<int> g_cus[kMaxDevices];
+std::atomic<long long> g_lds[kMaxDevices];
+}  // namespace
+
+int current_device_info(DeviceInfo *info) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CCE_ERR_LAUNCH;
+  info->device = dev;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cus = g_cus[dev].load(std::memory_order_relaxed);
+    const long long lds = g_lds[dev].load(std::memory_order_relaxed);
+    if (cus > 0 && lds > 0) {
+      info->num_cus = cus;
+      info->lds_per_block = (size_t)lds;
+      return CCE_OK;
+    }
+  }
+  int cus = 0, lds = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      cus < 1 || lds < 1)
+    return CCE_ERR_LAUNCH;
+  info->num_cus = cus;
+  info->lds_per_block = (size_t)lds;
+  if (dev >= 0 && dev < kMaxDevices) {
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+    g_lds[dev].store(lds, std::memory_order_relaxed);
+  }
+  return CCE_OK;
+}
+
+}  // namespace cce
+
+static bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+static bool is_finite_f(float v) { return isfinite(v); }
+
+extern "C" {
+
+const char *cce_status_string(int status) {
+  switch (status) {
+    case CCE_OK: return "success";
+    case CCE_ERR_NULL: return "a required pointer is NULL";
+    case CCE_ERR_SHAPE: return "a size is non-positive or the output would be empty";
+    case CCE_ERR_UNSUPPORTED: return "shape or parameter outside the supported set";
+    case CCE_ERR_ALIGN: return "a tensor pointer is not 4-byte aligned";
+    case CCE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case CCE_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    case CCE_ERR_TOO_LARGE: return "problem too large for 32-bit index arithmetic";
+    default: return "unknown status";
+  }
+}
+
+int cce_version(void) { return 100; }
+
+int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N, int C_in,
+                       int H, int W, int C_out, int k, void *stream) {
+  if (!x || !w || !y) return CCE_ERR_NULL;
+  if (N < 1 || C_in < 1 || C_out < 1 || k < 1 || H < k || W < k) return CCE_ERR_SHAPE;
+  if (C_in != 8 || C_out != 64 || k != 3) return CCE_ERR_UNSUPPORTED;
+  if (W > 1024) return CCE_ERR_UNSUPPORTED;
+  if (!aligned4(x) || !aligned4(w) || !aligned4(y) || (b && !aligned4(b))) return CCE_ERR_ALIGN;
+  const long long P = (long long)(H - 2) * (W - 2);
+  if ((long long)N * P >= (1LL << 31) || (long long)N * H >= (1LL << 31) ||
+      (long long)N * C_in * H * W >= (1LL << 40))
+    return CCE_ERR_TOO_LARGE;
+  return cce::launch_conv2d_relu_hswish(x, w, b, y, N, H, W, (hipStream_t)stream);
+}
+
+int conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b, const float *s,
+                                float *y, int N, int C_in, int D, int H, int W, int C_out, int k,
+                                float negative_slope, float clamp_lo, float clamp_hi,
+                                void *stream) {
+  if (!x || !w || !s || !y) return CCE_ERR_NULL;
+  if (N < 1 || C_in < 1 || C_out < 1 || k < 1 || D < k || H < k || W < k) return CCE_ERR_SHAPE;
+  if (C_in != 8 || C_out != 64 || k != 3) return CCE_ERR_UNSUPPORTED;
+  if (W > 512) return CCE_ERR_UNSUPPORTED;
+  if (!is_finite_f(negative_slope) || !is_finite_f(clamp_lo) || !is_finite_f(clamp_hi) || clamp_lo > clamp_hi)
+    return CCE_ERR_UNSUPPORTED;
+  if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(s) || (b && !aligned4(b)))
+    return CCE_ERR_ALIGN;
+  const long long outs = (long long)N * C_out * (D - 2) * (H - 2) * (W - 2);
+  if (outs >= (1LL << 31) || (long long)N * (D - 2) * (H - 2) >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
+  return cce::launch_conv3d_lrelu_add_clamp_gelu(x, w, b, s, y, N, D, H, W, negative_slope,
+                                                 clamp_lo, clamp_hi, (hipStream_t)stream);
+}
+
+static int convT_check_shape(int N, int C_in, int H, int W, int C_out, int k, int stride, int pad,
+                             int pool_k, int pool_s) {
+  if (N < 1 || C_in < 1 || C_out < 1 || k < 1 || H < 1 || W < 1 || stride < 1 || pad < 0 ||
+      pool_k < 1 || pool_s < 1)
+    return CCE_ERR_SHAPE;
+  const long long Ho = (long long)(H - 1) * stride - 2LL * pad + k;
+  const long long Wo = (long long)(W - 1) * stride - 2LL * pad + k;
+  if (Ho < pool_k || Wo < pool_k) return CCE_ERR_SHAPE;
+  if (C_in != 64 || C_out != 64 || k != 3 || stride != 1 || pad != 1 || pool_k != 2 || pool_s != 2)
+    return CCE_ERR_UNSUPPORTED;
+  if ((long long)N * C_in * H * W >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
+  return CCE_OK;
+}
+
+size_t convT2d_pool_htanh_mean_tanh_workspace_bytes(int N, int C_in, int H, int W, int C_out,
+                                                    int k, int stride, int pad, int pool_k,
+                                                    int pool_s) {
+  if (convT_check_shape(N, C_in, H, W, C_out, k, stride, pad, pool_k, pool_s) != CCE_OK) return 0;
+  return cce::convT_workspace_bytes(N, H, W);
+}
+
+int convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b, float *y, int N,
+                                 int C_in, int H, int W, int C_out, int k, int stride, int pad,
+                                 int pool_k, int pool_s, float htanh_lo, float htanh_hi,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  if (!x || !w || !y) return CCE_ERR_NULL;
+  const int st = convT_check_shape(N, C_in, H, W, C_out, k, stride, pad, pool_k, pool_s);
+  if (st != CCE_OK) return st;
+  if (!is_finite_f(htanh_lo) || !is_finite_f(htanh_hi) || htanh_lo > htanh_hi) return CCE_ERR_UNSUPPORTED;
+  if (!aligned4(x) || !aligned4(w) || !aligned4(y) || (b && !aligned4(b))) return CCE_ERR_ALIGN;
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 ||
+      workspace_bytes < cce::convT_workspace_bytes(N, H, W))
+    return CCE_ERR_WORKSPACE;
+  return cce::launch_convT2d_pool_htanh_mean_tanh(x, w, b, y, N, H, W, htanh_lo, htanh_hi,
+                                                  workspace, (hipStream_t)stream);
+}
+
+}  // extern "C"

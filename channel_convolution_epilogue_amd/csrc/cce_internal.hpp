@@ -1,0 +1,41 @@
+// Internal launch entry points of libcce (host side).  The extern "C" API in
+// cce_api.cpp validates every argument and then calls these; they pick the
+// kernel instance, grid and LDS size and enqueue one launch on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "cce.h"
+
+namespace cce {
+
+// Properties of the current device that size the persistent grids.
+struct DeviceInfo {
+  int device;
+  int num_cus;
+  size_t lds_per_block;
+};
+int current_device_info(DeviceInfo *info);  // CCE_OK or CCE_ERR_LAUNCH
+
+// Conv2d 3x3 (8 -> 64) + ReLU + HardSwish.  Arguments already validated.
+int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
+                              int H, int W, hipStream_t stream);
+
+// Conv3d 3x3x3 (8 -> 64) + LeakyReLU + add + clamp + GELU.  Validated.
+int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,
+                                       const float *s, float *y, int N, int D, int H, int W,
+                                       float slope, float lo, float hi, hipStream_t stream);
+
+// ConvTranspose2d 3x3 s1 p1 (64 -> 64) + MaxPool 2x2 + Hardtanh + mean + tanh.
+size_t convT_workspace_bytes(int N, int H, int W);
+int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b, float *y,
+                                        int N, int H, int W, float lo, float hi, void *workspace,
+                                        hipStream_t stream);
+
+// Map the runtime's last error after a launch onto a cce_status.
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? CCE_OK : CCE_ERR_LAUNCH;
+}
+
+}  // namespace cce

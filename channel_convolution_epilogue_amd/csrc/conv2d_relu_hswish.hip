@@ -1,0 +1,245 @@
+// Conv2d 3x3, 8 -> 64 channels, stride 1, padding 0, + bias -> ReLU -> HardSwish,
+// fused in one gfx950 kernel (POPCORNBENCH Kimi-K2.6 l2_p57: its model is
+// Conv2d(8, 64, 3) followed by ReLU and HardSwish x * clamp((x + 3) / 6, 0, 1)).
+//
+// Design (MI355X-first, not the page's one-thread-per-output CUDA tiling):
+//  * Implicit GEMM on the fp32 matrix cores: M = output pixels, N = the 64
+//    output channels, K = 8 channels x 9 taps = 72.  Packed fp32 VALU math is
+//    not used, so the matrix cores are the only units that reach the fp32
+//    peak; the contraction is dense enough (72 x 64 per pixel) to feed them.
+//  * Output pixels are numbered flat over (n, h, w) and cut into tiles of
+//    512.  A flat numbering keeps every lane's four result pixels 16-byte
+//    aligned even though the 126-wide rows are not, so results leave as
+//    16-byte stores, and no tile is ragged except the last one.
+//  * A tile's input rows (all 8 channels, full width) are staged in LDS once;
+//    each 16-pixel block then reads one A value per lane per K-step straight
+//    from LDS.  The K order puts the four lanes groups on four channels and
+//    one (channel half, kh, kw) per step, so the step's LDS offset is the same
+//    for all lanes.
+//  * The whole weight (72 x 64) lives in 72 VGPRs per lane, loaded once per
+//    workgroup; workgroups are persistent and take a contiguous run of tiles,
+//    so consecutive tiles (which share input rows) stay on one XCD's L2.
+//  * Bias is the accumulator's initial value; ReLU and HardSwish are applied
+//    in registers before the store: the conv result never reaches memory.
+#include "cce_device.hpp"
+#include "cce_internal.hpp"
+
+namespace cce {
+namespace {
+
+constexpr int CI = 8, CO = 64, KS = 3, TAPS = KS * KS;
+constexpr int KSTEPS = (CI / 4) * TAPS;  // 18 steps of 4 taps
+constexpr int NT = CO / 16;              // 4 channel blocks of 16
+constexpr int WAVES = 4, THREADS = 64 * WAVES;
+constexpr int MT_BATCH = 2;              // 16-pixel blocks in flight per wave
+
+struct Conv2dArgs {
+  const float *__restrict__ x;
+  const float *__restrict__ w;
+  const float *__restrict__ b;
+  float *__restrict__ y;
+  int H, W, Wo;
+  int P;         // output pixels per image plane, (H-2)*(W-2)
+  int Q;         // output pixels over the batch, N*P
+  int ntiles;    // ceil(Q / tile)
+  int chstride;  // floats between channel planes in LDS
+};
+
+__device__ __forceinline__ float relu_hswish(float v) {
+  const float r = fmaxf(v, 0.0f);
+  return r * fminf((r + 3.0f) * (1.0f / 6.0f), 1.0f);
+}
+
+// MT_WAVE: 16-pixel blocks per wave per tile (tile = 16 * MT_WAVE * WAVES pixels).
+// VLOAD: W % 4 == 0 (16-byte row loads).  VSTORE: P % 4 == 0 and y 16-byte aligned.
+template <int MT_WAVE, bool VLOAD, bool VSTORE>
+__global__ __launch_bounds__(THREADS) void conv2d_relu_hswish_kernel(Conv2dArgs a) {
+  constexpr int TILE = 16 * MT_WAVE * WAVES;
+  extern __shared__ float lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+
+  // B operand for every K-step and channel block: B[k][n] = w[o][ci][kh][kw]
+  // with o = 16 nt + col, ci = 4 * half + g, step = (half, kh, kw).
+  float wr[KSTEPS][NT];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int o = 16 * nt + col, ci = 4 * (s / TAPS) + g;
+      wr[s][nt] = a.w[(o * CI + ci) * TAPS + (s % TAPS)];
+    }
+  float bias[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
+
+  const int t_begin = (int)(((long long)blockIdx.x * a.ntiles) / gridDim.x);
+  const int t_end = (int)(((long long)(blockIdx.x + 1) * a.ntiles) / gridDim.x);
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int q0 = t * TILE;
+    const int qlast = min(q0 + TILE, a.Q) - 1;
+    const int n0 = q0 / a.P, n1 = qlast / a.P;
+    // Input rows are numbered r = n * H + h; the tile needs rows r_first..r_last.
+    const int r_first = n0 * a.H + (q0 - n0 * a.P) / a.Wo;
+    const int r_last = n1 * a.H + (qlast - n1 * a.P) / a.Wo + (KS - 1);
+    const int R = r_last - r_first + 1;
+
+    __syncthreads();  // the previous tile's LDS reads are done
+    {
+      const int cw = VLOAD ? (a.W >> 2) : a.W;  // copy units per row
+      const int tpr = cw < THREADS ? cw : THREADS;
+      const int rpp = THREADS / tpr;
+      const int my_row = tid / tpr, my_col = tid - my_row * tpr;
+      if (my_row < rpp) {
+        for (int ri = my_row; ri < CI * R; ri += rpp) {
+          const int ci = ri / R, rr = ri - ci * R;
+          const int r = r_first + rr, n = r / a.H, hh = r - n * a.H;
+          const float *src = a.x + (((size_t)n * CI + ci) * a.H + hh) * a.W;
+          float *dst = lds + ci * a.chstride + rr * a.W;
+          if (VLOAD) {
+            for (int c = my_col; c < cw; c += tpr)
+              *reinterpret_cast<v4f *>(dst + 4 * c) = *reinterpret_cast<const v4f *>(src + 4 * c);
+          } else {
+            for (int c = my_col; c < cw; c += tpr) dst[c] = src[c];
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+#pragma unroll 1
+    for (int mb = 0; mb < MT_WAVE; mb += MT_BATCH) {
+      int base[MT_BATCH];
+#pragma unroll
+      for (int j = 0; j < MT_BATCH; ++j) {
+        int q = q0 + 16 * (wave * MT_WAVE + mb + j) + col;
+        q = min(q, a.Q - 1);  // lanes past the end read a valid pixel; their results are dropped
+        const int n = q / a.P, p = q - n * a.P, h = p / a.Wo, w = p - h * a.Wo;
+        base[j] = g * a.chstride + (n * a.H + h - r_first) * a.W + w;
+      }
+      v4f acc[MT_BATCH][NT];
+#pragma unroll
+      for (int j = 0; j < MT_BATCH; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[j][nt] = splat4(bias[nt]);
+
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const int tap = s % TAPS;
+        const int off = (s / TAPS) * 4 * a.chstride + (tap / KS) * a.W + (tap % KS);
+        float av[MT_BATCH];
+#pragma unroll
+        for (int j = 0; j < MT_BATCH; ++j) av[j] = lds[base[j] + off];
+#pragma unroll
+        for (int j = 0; j < MT_BATCH; ++j)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[j][nt] = mfma16x16x4(av[j], wr[s][nt], acc[j][nt]);
+      }
+
+#pragma unroll
+      for (int j = 0; j < MT_BATCH; ++j) {
+        const int qq = q0 + 16 * (wave * MT_WAVE + mb + j) + 4 * g;  // this lane's first pixel
+        if (qq >= a.Q) continue;
+        if (VSTORE) {
+          // P % 4 == 0 and Q % 4 == 0: the four pixels are in one plane and all valid.
+          const int n = qq / a.P, p = qq - n * a.P;
+          float *dst = a.y + (size_t)n * CO * a.P + p;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            v4f v = acc[j][nt];
+            v.x = relu_hswish(v.x);
+            v.y = relu_hswish(v.y);
+            v.z = relu_hswish(v.z);
+            v.w = relu_hswish(v.w);
+            store4(dst + (size_t)(16 * nt + col) * a.P, v);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int qr = qq + r;
+            if (qr >= a.Q) break;
+            const int n = qr / a.P, p = qr - n * a.P;
+            float *dst = a.y + (size_t)n * CO * a.P + p;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              dst[(size_t)(16 * nt + col) * a.P] = relu_hswish(acc[j][nt][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MT_WAVE, bool VL, bool VS>
+int launch_instance(const Conv2dArgs &a, int R_max, hipStream_t stream) {
+  constexpr int TILE = 16 * MT_WAVE * WAVES;
+  (void)TILE;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
+  const size_t lds_bytes = (size_t)CI * a.chstride * sizeof(float);
+  (void)R_max;
+  if (lds_bytes > dev.lds_per_block) return CCE_ERR_UNSUPPORTED;
+  auto kern = conv2d_relu_hswish_kernel<MT_WAVE, VL, VS>;
+  if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds_bytes) != hipSuccess)
+    return CCE_ERR_LAUNCH;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, THREADS, lds_bytes) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  int grid = dev.num_cus * per_cu;
+  if (grid > a.ntiles) grid = a.ntiles;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds_bytes, stream, a);
+  return launch_status();
+}
+
+}  // namespace
+
+int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
+                              int H, int W, hipStream_t stream) {
+  Conv2dArgs a;
+  a.x = x;
+  a.w = w;
+  a.b = b;
+  a.y = y;
+  a.H = H;
+  a.W = W;
+  a.Wo = W - (KS - 1);
+  const int Ho = H - (KS - 1);
+  a.P = Ho * a.Wo;
+  a.Q = N * a.P;
+
+  DeviceInfo dev;
+  if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
+  // Small problems use 128-pixel tiles so that every CU gets work.
+  const bool small = (a.Q + 511) / 512 < 2 * dev.num_cus;
+  const int tile = small ? 128 : 512;
+  a.ntiles = (a.Q + tile - 1) / tile;
+
+  // Upper bound on the input rows one tile touches: output rows spanned plus
+  // (k - 1) halo rows for every image the tile reaches into.
+  const int rows_spanned = (tile - 1 + a.Wo - 1) / a.Wo + 1;
+  const int images_spanned = (tile - 1 + a.P - 1) / a.P + 1;
+  int R_max = rows_spanned + (KS - 1) * images_spanned;
+  if (R_max > N * H) R_max = N * H;
+  // Channel planes padded so the four lane groups (four channels) of a read
+  // start 16 banks apart.
+  int plane = R_max * W;
+  a.chstride = plane + ((16 - plane % 64) + 64) % 64;
+
+  const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  const bool vs = (a.P % 4 == 0) && ((uintptr_t)y % 16 == 0);
+  if (small) {
+    if (vl) return vs ? launch_instance<2, true, true>(a, R_max, stream)
+                      : launch_instance<2, true, false>(a, R_max, stream);
+    return vs ? launch_instance<2, false, true>(a, R_max, stream)
+              : launch_instance<2, false, false>(a, R_max, stream);
+  }
+  if (vl) return vs ? launch_instance<8, true, true>(a, R_max, stream)
+                    : launch_instance<8, true, false>(a, R_max, stream);
+  return vs ? launch_instance<8, false, true>(a, R_max, stream)
+            : launch_instance<8, false, false>(a, R_max, stream);
+}
+
+}  // namespace cce

@@ -1,0 +1,143 @@
+/*
+ * cce.h -- C ABI of the fused small-channel convolution + epilogue library
+ * (libcce.so, HIP kernels for AMD MI355X / gfx950).
+ *
+ * Three operators, each one kernel launch that reads its input and weights
+ * from device memory and writes only its final output (the convolution
+ * result never reaches device memory):
+ *
+ *   conv2d_relu_hswish            Conv2d k x k (stride 1, padding 0) -> ReLU -> HardSwish
+ *   conv3d_lrelu_add_clamp_gelu   Conv3d k^3 (stride 1, padding 0) -> LeakyReLU -> + s[c]
+ *                                 -> clamp -> exact GELU
+ *   convT2d_pool_htanh_mean_tanh  ConvTranspose2d -> MaxPool2d -> Hardtanh -> mean over
+ *                                 (H, W) -> tanh
+ *
+ * The operators are the three models of the POPCORNBENCH Kimi-K2.6 level-2
+ * transcripts l2_p57, l2_p90 and l2_p10 (each entry point names its page).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers to contiguous fp32 data, in the
+ *    layouts stated per function (NCHW / NCDHW activations).  The caller owns
+ *    every buffer; the library never allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously on it; the call returns before the
+ *    kernel runs.
+ *  - Arguments are validated on the host before any HIP call.  An invalid or
+ *    unsupported call returns a negative cce_status and launches nothing.  A
+ *    failed launch returns CCE_ERR_LAUNCH.  Faults inside a running kernel
+ *    surface, as usual for HIP, at the caller's next synchronisation.
+ *  - Calls on different streams may run concurrently, except that one
+ *    convT2d workspace must not be used by two calls at the same time.
+ *  - Arithmetic is fp32 (products accumulated in fp32 by the matrix cores).
+ *    Results match a double-precision evaluation of the definitions within
+ *    |gpu - ref| <= 1e-4 + 1e-4 * |ref| per element.
+ */
+#ifndef CCE_H
+#define CCE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CCE_OK = 0,
+  CCE_ERR_NULL = -1,        /* a required pointer is NULL */
+  CCE_ERR_SHAPE = -2,       /* a size is non-positive, or the output would be empty */
+  CCE_ERR_UNSUPPORTED = -3, /* valid shape outside the set the kernels are built for */
+  CCE_ERR_ALIGN = -4,       /* a tensor pointer is not 4-byte aligned */
+  CCE_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or smaller than required */
+  CCE_ERR_LAUNCH = -6,      /* the HIP runtime rejected the launch (no device, wrong arch ...) */
+  CCE_ERR_TOO_LARGE = -7    /* an index would overflow the kernels' 32-bit arithmetic */
+} cce_status;
+
+/* Human-readable text for a cce_status value (static storage, never NULL). */
+const char *cce_status_string(int status);
+
+/* Library ABI version: 100 * major + minor. */
+int cce_version(void);
+
+/*
+ * y = HardSwish(ReLU(conv2d(x, w) + b))           -- page l2_p57
+ *
+ *   x  [N][C_in][H][W]                      input
+ *   w  [C_out][C_in][k][k]                  conv weight (torch Conv2d layout)
+ *   b  [C_out] or NULL (NULL = zero bias)   conv bias
+ *   y  [N][C_out][H-k+1][W-k+1]             output
+ *
+ * z[n,o,h,w] = b[o] + sum_{i,kh,kw} x[n,i,h+kh,w+kw] * w[o,i,kh,kw]  (stride 1,
+ * padding 0, the defaults the page's problem uses), r = max(z, 0),
+ * y = r * clamp((r + 3) / 6, 0, 1).
+ *
+ * Supported: C_in = 8, C_out = 64, k = 3, any N >= 1, H, W >= 3 with the
+ * input tile of 8 channel rows fitting in LDS (W <= 1024), N*(H-2)*(W-2)
+ * < 2^31.  Anything else returns CCE_ERR_UNSUPPORTED.
+ */
+int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N, int C_in,
+                       int H, int W, int C_out, int k, void *stream);
+
+/*
+ * y = GELU(clamp(LeakyReLU(conv3d(x, w) + b, slope) + s[o], lo, hi))   -- page l2_p90
+ *
+ *   x  [N][C_in][D][H][W]                   input
+ *   w  [C_out][C_in][k][k][k]               conv weight (torch Conv3d layout)
+ *   b  [C_out] or NULL (NULL = zero bias)   conv bias
+ *   s  [C_out] (the [C_out,1,1,1] sum_tensor), required
+ *   y  [N][C_out][D-k+1][H-k+1][W-k+1]      output
+ *
+ * LeakyReLU(t) = t for t >= 0, slope * t otherwise; clamp to [lo, hi];
+ * GELU(t) = 0.5 t (1 + erf(t / sqrt 2)) (exact, not the tanh form).
+ *
+ * Supported: C_in = 8, C_out = 64, k = 3, any N >= 1, D, H, W >= 3 with
+ * W <= 512, lo <= hi, all three scalars finite, N*C_out*(D-2)*(H-2)*(W-2)
+ * < 2^31.  Anything else returns CCE_ERR_UNSUPPORTED (or CCE_ERR_SHAPE).
+ */
+int conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b, const float *s,
+                                float *y, int N, int C_in, int D, int H, int W, int C_out, int k,
+                                float negative_slope, float clamp_lo, float clamp_hi, void *stream);
+
+/*
+ * y[n,o] = tanh(mean_{ph,pw} Hardtanh(MaxPool2d(convT2d(x, w) + b)))   -- page l2_p10
+ *
+ *   x  [N][C_in][H][W]                      input
+ *   w  [C_in][C_out][k][k]                  transposed-conv weight (torch layout)
+ *   b  [C_out] or NULL (NULL = zero bias)
+ *   y  [N][C_out] (the [N,C_out,1,1] result)
+ *
+ * The transposed conv (stride s, padding p, output padding 0) has output
+ * size Ho = (H-1)*s - 2p + k; at stride 1, padding 1 it equals a correlation
+ * with the kernel flipped in both spatial axes and its channel axes swapped.
+ * MaxPool2d(pool_k, pool_s) has output floor((Ho - pool_k) / pool_s) + 1 per
+ * axis; Hardtanh clamps to [htanh_lo, htanh_hi]; the mean divides by the
+ * pooled element count.
+ *
+ * Workspace: device memory of at least
+ * convT2d_pool_htanh_mean_tanh_workspace_bytes(...) bytes, 256-byte
+ * aligned, ALL ZERO before the first call that uses it.  Each call leaves it
+ * in a state valid for the next call of any shape, so zero it once, when it
+ * is allocated.  It holds per-image completion counters and per-tile
+ * partial sums; one workspace serves one call at a time.
+ *
+ * Supported: C_in = C_out = 64, k = 3, stride = 1, pad = 1, pool_k =
+ * pool_s = 2, H, W >= 2, htanh_lo <= htanh_hi (finite), N >= 1,
+ * N*C_in*H*W < 2^31.  Anything else returns CCE_ERR_UNSUPPORTED (or
+ * CCE_ERR_SHAPE).  The result is deterministic: partial sums are combined
+ * in a fixed order.
+ */
+int convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b, float *y, int N,
+                                 int C_in, int H, int W, int C_out, int k, int stride, int pad,
+                                 int pool_k, int pool_s, float htanh_lo, float htanh_hi,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace the call above needs for these sizes (0 if the sizes
+ * are invalid or unsupported). */
+size_t convT2d_pool_htanh_mean_tanh_workspace_bytes(int N, int C_in, int H, int W, int C_out,
+                                                    int k, int stride, int pad, int pool_k,
+                                                    int pool_s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCE_H */

@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute launched).
+
+* libcce.so loads and exports every function include/cce.h declares.
+* Argument validation returns the documented status before any HIP call:
+  every case here fails validation, so nothing reaches the runtime.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import channel_convolution_epilogue_amd as cce
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "cce.h"
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, ELAUNCH, ETOOBIG = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = 0x10000  # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-zA-Z_][a-zA-Z0-9_]*)\s*\(", text)) -
+                  {"if", "defined", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cce.load()
+
+
+def test_header_declares_the_api():
+    assert declared_functions() == sorted(cce.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(str(cce.library_path()))
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for st in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, ELAUNCH, ETOOBIG):
+        s = cce.status_string(st)
+        assert s and s != "unknown status"
+    assert cce.status_string(12345) == "unknown status"
+    assert lib.cce_version() == 100
+
+
+def c2(lib, x=FAKE, w=FAKE, b=None, y=FAKE, N=1, C_in=8, H=16, W=16, C_out=64, k=3):
+    return lib.conv2d_relu_hswish(x, w, b, y, N, C_in, H, W, C_out, k, None)
+
+
+def test_conv2d_validation(lib):
+    assert c2(lib, x=None) == ENULL
+    assert c2(lib, w=None) == ENULL
+    assert c2(lib, y=None) == ENULL
+    assert c2(lib, N=0) == ESHAPE
+    assert c2(lib, H=2) == ESHAPE
+    assert c2(lib, W=-5) == ESHAPE
+    assert c2(lib, C_in=3) == EUNSUP
+    assert c2(lib, C_out=32) == EUNSUP
+    assert c2(lib, k=5) == EUNSUP
+    assert c2(lib, W=2048) == EUNSUP
+    assert c2(lib, x=FAKE + 2) == EALIGN
+    assert c2(lib, b=FAKE + 1) == EALIGN
+    assert c2(lib, N=1 << 20, H=1024, W=1024) == ETOOBIG
+
+
+def c3(lib, x=FAKE, w=FAKE, b=None, s=FAKE, y=FAKE, N=1, C_in=8, D=5, H=9, W=9, C_out=64, k=3,
+       slope=0.2, lo=-1.0, hi=1.0):
+    return lib.conv3d_lrelu_add_clamp_gelu(x, w, b, s, y, N, C_in, D, H, W, C_out, k, slope, lo, hi,
+                                           None)
+
+
+def test_conv3d_validation(lib):
+    assert c3(lib, s=None) == ENULL
+    assert c3(lib, x=None) == ENULL
+    assert c3(lib, D=2) == ESHAPE
+    assert c3(lib, C_in=4) == EUNSUP
+    assert c3(lib, W=600) == EUNSUP
+    assert c3(lib, lo=1.0, hi=-1.0) == EUNSUP
+    assert c3(lib, slope=float("nan")) == EUNSUP
+    assert c3(lib, hi=float("inf")) == EUNSUP
+    assert c3(lib, s=FAKE + 2) == EALIGN
+    assert c3(lib, N=1 << 16, D=64, H=128, W=128) == ETOOBIG
+
+
+def ct(lib, x=FAKE, w=FAKE, b=None, y=FAKE, N=2, C_in=64, H=16, W=16, C_out=64, k=3, stride=1,
+       pad=1, pk=2, ps=2, lo=-1.0, hi=1.0, ws=FAKE, ws_bytes=1 << 20):
+    return lib.convT2d_pool_htanh_mean_tanh(x, w, b, y, N, C_in, H, W, C_out, k, stride, pad, pk, ps,
+                                            lo, hi, ws, ws_bytes, None)
+
+
+def test_convT_validation(lib):
+    assert ct(lib, x=None) == ENULL
+    assert ct(lib, y=None) == ENULL
+    assert ct(lib, H=1) == ESHAPE  # conv output 1 x W is smaller than the 2 x 2 pool
+    assert ct(lib, stride=0) == ESHAPE
+    assert ct(lib, stride=2) == EUNSUP
+    assert ct(lib, pad=0) == EUNSUP
+    assert ct(lib, pk=3) == EUNSUP
+    assert ct(lib, C_in=32) == EUNSUP
+    assert ct(lib, lo=2.0, hi=1.0) == EUNSUP
+    assert ct(lib, w=FAKE + 2) == EALIGN
+    assert ct(lib, ws=None) == EWS
+    assert ct(lib, ws=FAKE + 16) == EWS  # must be 256-byte aligned
+    need = cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(2, 64, 16, 16, 64)
+    assert ct(lib, ws_bytes=need - 1) == EWS
+    assert ct(lib, N=1 << 12, H=1024, W=1024) == ETOOBIG
+
+
+def test_convT_workspace_size(lib):
+    # N counters (padded to 256 bytes) + N * tiles * 64 fp32 partial sums, tiles of
+    # 8 x 16 pooling windows.
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(16, 64, 256, 256, 64) == 256 + 16 * 128 * 256
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(128, 64, 256, 256, 64) == 512 + 128 * 128 * 256
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 64, 2, 2, 64) == 256 + 256
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 64, 16, 16, 64, stride=2) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 8, 8, 8)
+    w = torch.zeros(64, 8, 3, 3)
+    with pytest.raises(TypeError):
+        cce.conv2d_relu_hswish(x, w, None, out=torch.zeros(1, 64, 6, 6))

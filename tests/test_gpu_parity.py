@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: every element within |gpu - ref| <= 1e-4 + 1e-4 * |ref| (the fp32
+atol = rtol = 1e-4 tolerance of the l2_p90 problem statement), no NaN/Inf.
+Small cases compare every element and cover several tiles, ragged tails,
+odd sizes (scalar load/store paths), the minimum sizes and a NULL bias.
+Full-size workloads run in the launch configuration the benchmark times and
+are checked on sampled outputs the oracle computes one by one, plus
+properties that hold at any size (output range, determinism).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from conv_inputs import CONV2D, CONV3D, CONVT, make_inputs, workload_inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ATOL = RTOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def cce():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import channel_convolution_epilogue_amd as m
+    m.load()
+    return m
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(a).cuda()
+
+
+def assert_close(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
+    err = np.abs(got - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    bad = err > bound
+    if bad.any():
+        i = int(np.argmax(err - bound))
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside tolerance; worst at flat "
+                             f"{i}: gpu={got.reshape(-1)[i]!r} ref={ref.reshape(-1)[i]!r}")
+    print(f"{what}: max abs err {err.max():.3e} over {err.size} values", flush=True)
+
+
+def sample_indices(total, count, seed):
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, total, size=count, dtype=np.int64)
+    return np.unique(np.concatenate([idx, [0, 1, total // 2, total - 2, total - 1]]))
+
+
+# ---------------------------------------------------------------------------
+# Conv2d + ReLU + HardSwish
+# ---------------------------------------------------------------------------
+
+CONV2D_SMALL = [  # (N, H, W, bias)   covers: tiles, image-crossing tiles, odd sizes, minimum
+    (2, 20, 20, True),
+    (3, 37, 29, True),   # W % 4 != 0, plane % 4 != 0: scalar loads and stores
+    (1, 3, 3, True),     # one output pixel
+    (5, 128, 128, True),
+    (4, 11, 130, False),  # NULL bias, wide rows
+    (7, 64, 66, True),   # 7 images: tiles straddle image boundaries, ragged last tile
+]
+
+
+@pytest.mark.parametrize("N,H,W,bias", CONV2D_SMALL)
+def test_conv2d_small(cce, N, H, W, bias):
+    p = make_inputs(CONV2D, seed=100 + N, N=N, C_in=8, H=H, W=W, C_out=64, k=3)
+    b = p["b"] if bias else None
+    y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(b))
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), O.conv2d_relu_hswish(p["x"], p["w"], b), f"conv2d N={N} {H}x{W}")
+
+
+def test_conv2d_workload_n8_full(cce):
+    shape, p = workload_inputs("conv2d_relu_hswish_n8", seed=0)
+    y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), O.conv2d_relu_hswish(p["x"], p["w"], p["b"]), "conv2d n8 full")
+
+
+def test_conv2d_workload_n128_sampled(cce):
+    shape, p = workload_inputs("conv2d_relu_hswish_n128", seed=0)
+    y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert yh.shape == (128, 64, 126, 126)
+    assert np.all(np.isfinite(yh)) and yh.min() >= 0.0  # HardSwish(ReLU(.)) >= 0
+    idx = sample_indices(yh.size, 20000, 1)
+    ref = O.conv2d_relu_hswish_at(p["x"], p["w"], p["b"], idx)
+    assert_close(yh.reshape(-1)[idx], ref, "conv2d n128 sampled")
+
+
+# ---------------------------------------------------------------------------
+# Conv3d + LeakyReLU + add + clamp + GELU
+# ---------------------------------------------------------------------------
+
+# GELU on [-1, 1] spans [min_t t*Phi(t), GELU(1)].
+GELU_LO, GELU_HI = -0.16997120748, 0.84134474607
+
+
+CONV3D_SMALL = [  # (N, D, H, W, bias)
+    (2, 5, 12, 10, True),
+    (1, 3, 3, 3, True),     # one output voxel
+    (2, 6, 21, 19, True),   # ragged row tiles, odd widths: scalar paths
+    (3, 4, 22, 64, False),  # NULL bias, 4 row tiles of 8 (last one 4 rows)
+    (1, 16, 64, 64, True),  # one image of the Conv3d workload
+]
+
+
+@pytest.mark.parametrize("N,D,H,W,bias", CONV3D_SMALL)
+def test_conv3d_small(cce, N, D, H, W, bias):
+    p = make_inputs(CONV3D, seed=200 + N, N=N, C_in=8, D=D, H=H, W=W, C_out=64, k=3)
+    s = p["s"] * 20  # wider than the workload's 0.02 so the add visibly matters
+    b = p["b"] if bias else None
+    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(b), dev(s), 0.2, -1.0, 1.0)
+    torch.cuda.synchronize()
+    ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], b, s, 0.2, -1.0, 1.0)
+    assert_close(y.cpu().numpy(), ref, f"conv3d N={N} {D}x{H}x{W}")
+
+
+def test_conv3d_other_epilogue_parameters(cce):
+    p = make_inputs(CONV3D, seed=7, N=2, C_in=8, D=5, H=10, W=12, C_out=64, k=3)
+    x, w, b, s = (dev(p[k]) for k in "xwbs")
+    for slope, lo, hi in [(0.01, -0.5, 0.75), (1.0, -3.0, 3.0), (0.2, 0.0, 0.0)]:
+        y = cce.conv3d_lrelu_add_clamp_gelu(x, w, b, s, slope, lo, hi)
+        torch.cuda.synchronize()
+        ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"], slope, lo, hi)
+        assert_close(y.cpu().numpy(), ref, f"conv3d slope={slope} clamp=[{lo},{hi}]")
+
+
+def test_conv3d_workload_n128_sampled(cce):
+    shape, p = workload_inputs("conv3d_lrelu_add_clamp_gelu_n128", seed=0)
+    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]),
+                                        shape["slope"], shape["lo"], shape["hi"])
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert yh.shape == (128, 64, 14, 62, 62)
+    assert np.all(np.isfinite(yh))
+    assert yh.min() >= GELU_LO - 1e-6 and yh.max() <= GELU_HI + 1e-6
+    idx = sample_indices(yh.size, 20000, 2)
+    ref = O.conv3d_lrelu_add_clamp_gelu_at(p["x"], p["w"], p["b"], p["s"], idx, shape["slope"],
+                                           shape["lo"], shape["hi"])
+    assert_close(yh.reshape(-1)[idx], ref, "conv3d n128 sampled")
+
+
+# ---------------------------------------------------------------------------
+# ConvTranspose2d + MaxPool + Hardtanh + mean + tanh
+# ---------------------------------------------------------------------------
+
+CONVT_SMALL = [  # (N, H, W, bias)
+    (2, 34, 34, True),    # 2 x 2 tiles, ragged
+    (3, 37, 23, True),    # odd sizes: floor pooling drops the last row / column
+    (2, 2, 2, True),      # one pooling window
+    (1, 16, 32, False),   # exactly one tile, NULL bias
+    (2, 64, 96, True),
+]
+
+
+@pytest.mark.parametrize("N,H,W,bias", CONVT_SMALL)
+def test_convT_small(cce, N, H, W, bias):
+    p = make_inputs(CONVT, seed=300 + N, N=N, C_in=64, H=H, W=W, C_out=64, k=3)
+    b = p["b"] if bias else None
+    y = cce.convT2d_pool_htanh_mean_tanh(dev(p["x"]), dev(p["w"]), dev(b))
+    torch.cuda.synchronize()
+    ref = O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], b)
+    assert_close(y.cpu().numpy()[:, :, 0, 0], ref, f"convT N={N} {H}x{W}")
+
+
+def test_convT_hardtanh_bounds_and_saturation(cce):
+    p = make_inputs(CONVT, seed=9, N=2, C_in=64, H=20, W=18, C_out=64, k=3)
+    x, w = dev(p["x"]), dev(p["w"])
+    for lo, hi, scale in [(-0.25, 0.5, 1.0), (-1.0, 1.0, 8.0)]:
+        b = (p["b"] * scale).astype(np.float32)
+        y = cce.convT2d_pool_htanh_mean_tanh(x, w, dev(b), htanh_lo=lo, htanh_hi=hi)
+        torch.cuda.synchronize()
+        ref = O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], b, lo=lo, hi=hi)
+        assert_close(y.cpu().numpy()[:, :, 0, 0], ref, f"convT hardtanh [{lo},{hi}]")
+
+
+def test_convT_workspace_reuse_across_shapes_and_determinism(cce):
+    p1 = make_inputs(CONVT, seed=11, N=4, C_in=64, H=48, W=40, C_out=64, k=3)
+    p2 = make_inputs(CONVT, seed=12, N=2, C_in=64, H=18, W=70, C_out=64, k=3)
+    x1, w1, b1 = dev(p1["x"]), dev(p1["w"]), dev(p1["b"])
+    x2, w2, b2 = dev(p2["x"]), dev(p2["w"]), dev(p2["b"])
+    need = max(cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(4, 64, 48, 40, 64),
+               cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(2, 64, 18, 70, 64))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs1, outs2 = [], []
+    for _ in range(3):
+        outs1.append(cce.convT2d_pool_htanh_mean_tanh(x1, w1, b1, workspace=ws).cpu().numpy())
+        outs2.append(cce.convT2d_pool_htanh_mean_tanh(x2, w2, b2, workspace=ws).cpu().numpy())
+    for o in outs1[1:]:
+        assert np.array_equal(o, outs1[0]), "convT result not bitwise reproducible"
+    for o in outs2[1:]:
+        assert np.array_equal(o, outs2[0]), "convT result not bitwise reproducible"
+    assert_close(outs1[0][:, :, 0, 0], O.convT2d_pool_htanh_mean_tanh(p1["x"], p1["w"], p1["b"]), "convT reuse A")
+    assert_close(outs2[0][:, :, 0, 0], O.convT2d_pool_htanh_mean_tanh(p2["x"], p2["w"], p2["b"]), "convT reuse B")
+    # the kernel leaves the per-image counters at zero
+    torch.cuda.synchronize()
+    assert int(ws[:16].sum().item()) == 0
+
+
+@pytest.mark.parametrize("name,count", [("convT2d_pool_htanh_mean_tanh_n16", 48),
+                                        ("convT2d_pool_htanh_mean_tanh_n128", 32)])
+def test_convT_workload_sampled(cce, name, count):
+    shape, p = workload_inputs(name, seed=0)
+    y = cce.convT2d_pool_htanh_mean_tanh(dev(p["x"]), dev(p["w"]), dev(p["b"]))
+    y2 = cce.convT2d_pool_htanh_mean_tanh(dev(p["x"]), dev(p["w"]), dev(p["b"]))
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()[:, :, 0, 0]
+    assert np.array_equal(yh, y2.cpu().numpy()[:, :, 0, 0])
+    assert np.all(np.abs(yh) <= math.tanh(1.0) + 1e-6)
+    rng = np.random.default_rng(3)
+    idx = np.unique(np.concatenate([rng.integers(0, yh.size, count), [0, yh.size - 1]]))
+    ref = O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], idx)
+    assert_close(yh.reshape(-1)[idx], ref, f"{name} sampled")
