@@ -55,12 +55,124 @@ struct ConvTArgs {
   float *__restrict__ y;
   unsigned *tickets;  // [N] per-image completion counters (zero between calls)
   float *partials;    // [N][tiles_per_image][64]
+  const float *wprep; // prepared weight, NCHUNK x WS_FLOATS
   int H, W, PH, PW;
   int tiles_x, tiles_per_image;
   float lo, hi, inv_count;
 };
 
-__global__ __launch_bounds__(THREADS) void convT2d_pool_htanh_mean_tanh_kernel(ConvTArgs a) {
+// Per-chunk staging in 16-byte units.  The weight slice of chunk c is
+// contiguous in the prepared layout; the input tile's 32 interior columns of
+// each (channel, row) are four-aligned in the image (w0 % 32 == 0, W % 4 == 0)
+// and land on four-aligned LDS columns (XOFF + 1 = 4); the two halo columns
+// are single floats.
+constexpr int W4_PER_CHUNK = WS_FLOATS / 4;                        // 1152
+constexpr int W4_PT = (W4_PER_CHUNK + THREADS - 1) / THREADS;      // 5
+constexpr int XQ = TW / 4;                                         // 8 float4 per row
+constexpr int X4_PER_CHUNK = CC * XR * XQ;                         // 1152
+constexpr int X4_PT = (X4_PER_CHUNK + THREADS - 1) / THREADS;      // 5
+constexpr int XH_PER_CHUNK = CC * XR * 2;                          // 288 halo floats
+constexpr int XH_PT = (XH_PER_CHUNK + THREADS - 1) / THREADS;      // 2
+static_assert(XOFF + 1 == 4, "interior columns start 16-byte aligned in LDS");
+
+struct ChunkRegs {
+  v4f w4[W4_PT];
+  v4f x4[X4_PT];
+  float xh[XH_PT];
+};
+
+// Global -> registers for channel chunk c (issued a whole chunk ahead of use).
+// VEC: W % 4 == 0 and x 16-byte aligned, so each interior quad is one aligned
+// 16-byte load that is either wholly inside the row or wholly past its end.
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(const ConvTArgs &a, int n, int c, int h0, int w0, int tid,
+                                           ChunkRegs &r) {
+  const v4f *wsrc = reinterpret_cast<const v4f *>(a.wprep) + (size_t)c * W4_PER_CHUNK;
+#pragma unroll
+  for (int j = 0; j < W4_PT; ++j) {
+    const int i = tid + j * THREADS;
+    if (i < W4_PER_CHUNK) r.w4[j] = wsrc[i];
+  }
+  const float *xc = a.x + ((size_t)n * CI + CC * c) * a.H * a.W;
+#pragma unroll
+  for (int j = 0; j < X4_PT; ++j) {
+    const int i = tid + j * THREADS;
+    v4f v = splat4(0.0f);
+    if (i < X4_PER_CHUNK) {
+      const int row = i / XQ, q = i - row * XQ;  // row = cl * XR + rr
+      const int cl = row / XR, rr = row - cl * XR;
+      const int h = h0 - 1 + rr, wc = w0 + 4 * q;
+      if (h >= 0 && h < a.H) {
+        const float *src = xc + ((size_t)cl * a.H + h) * a.W + wc;
+        if (VEC) {
+          if (wc < a.W) v = *reinterpret_cast<const v4f *>(src);
+        } else {
+          if (wc < a.W) v.x = src[0];
+          if (wc + 1 < a.W) v.y = src[1];
+          if (wc + 2 < a.W) v.z = src[2];
+          if (wc + 3 < a.W) v.w = src[3];
+        }
+      }
+    }
+    r.x4[j] = v;
+  }
+#pragma unroll
+  for (int j = 0; j < XH_PT; ++j) {
+    const int i = tid + j * THREADS;
+    float v = 0.0f;
+    if (i < XH_PER_CHUNK) {
+      const int row = i >> 1, side = i & 1;
+      const int cl = row / XR, rr = row - cl * XR;
+      const int h = h0 - 1 + rr, wc = side ? w0 + TW : w0 - 1;
+      if (h >= 0 && h < a.H && wc >= 0 && wc < a.W) v = xc[((size_t)cl * a.H + h) * a.W + wc];
+    }
+    r.xh[j] = v;
+  }
+}
+
+// Registers -> LDS.
+__device__ __forceinline__ void store_chunk(float *xs, float *ws, int tid, const ChunkRegs &r) {
+#pragma unroll
+  for (int j = 0; j < W4_PT; ++j) {
+    const int i = tid + j * THREADS;
+    if (i < W4_PER_CHUNK) reinterpret_cast<v4f *>(ws)[i] = r.w4[j];
+  }
+#pragma unroll
+  for (int j = 0; j < X4_PT; ++j) {
+    const int i = tid + j * THREADS;
+    if (i < X4_PER_CHUNK) {
+      const int row = i / XQ, q = i - row * XQ;
+      const int cl = row / XR, rr = row - cl * XR;
+      *reinterpret_cast<v4f *>(&xs[cl * XCS + rr * XRS + XOFF + 1 + 4 * q]) = r.x4[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < XH_PT; ++j) {
+    const int i = tid + j * THREADS;
+    if (i < XH_PER_CHUNK) {
+      const int row = i >> 1, side = i & 1;
+      const int cl = row / XR, rr = row - cl * XR;
+      xs[cl * XCS + rr * XRS + (side ? XOFF + 1 + TW : XOFF)] = r.xh[j];
+    }
+  }
+}
+
+// Weight preparation (once per call, 36,864 floats): the flipped, channel-
+// swapped kernel in exactly the LDS B-operand order of every chunk,
+//   wprep[c][cb][tap'][lane][nt] = W[8c + 4cb + lane/16][16nt + lane%16][8 - tap'],
+// where tap' = 3 kh' + kw' and W's tap index 3 kh + kw = 8 - tap'.
+__global__ __launch_bounds__(THREADS) void convT_prepare_weight_kernel(const float *__restrict__ w,
+                                                                      float *__restrict__ wprep) {
+  const int p = blockIdx.x * THREADS + threadIdx.x;
+  if (p >= NCHUNK * WS_FLOATS) return;
+  const int nt = p & 3, lane = (p >> 2) & 63, rest = p >> 8;  // rest = (c * 2 + cb) * 9 + tap
+  const int tap = rest % 9, ccb = rest / 9;                    // ccb = c * 2 + cb
+  const int ci = 4 * ccb + (lane >> 4), o = 16 * nt + (lane & 15);
+  wprep[p] = w[((size_t)ci * CO + o) * 9 + (8 - tap)];
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kernel(ConvTArgs a) {
   __shared__ __attribute__((aligned(16))) float xs[XS_FLOATS];
   __shared__ __attribute__((aligned(16))) float ws[WS_FLOATS];
   __shared__ float red[WAVES][64];
@@ -84,30 +196,15 @@ __global__ __launch_bounds__(THREADS) void convT2d_pool_htanh_mean_tanh_kernel(C
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = splat4(0.0f);
 
+  ChunkRegs r;
+  load_chunk<VEC>(a, n, 0, h0, w0, tid, r);
+  store_chunk(xs, ws, tid, r);
+  __syncthreads();
+
 #pragma unroll 1
   for (int c = 0; c < NCHUNK; ++c) {
-    __syncthreads();  // previous chunk's LDS reads are done
-    // Input halo tile of channels 8c..8c+7, zero outside the image (padding 1).
-    for (int idx = tid; idx < CC * XR * XC; idx += THREADS) {
-      const int cl = idx / (XR * XC), rem = idx - cl * (XR * XC);
-      const int rr = rem / XC, cc = rem - rr * XC;
-      const int h = h0 - 1 + rr, wc = w0 - 1 + cc;
-      float v = 0.0f;
-      if (h >= 0 && h < a.H && wc >= 0 && wc < a.W)
-        v = a.x[(((size_t)n * CI + CC * c + cl) * a.H + h) * a.W + wc];
-      xs[cl * XCS + rr * XRS + XOFF + cc] = v;
-    }
-    // Weight slice, flipped and swapped into B-operand order:
-    // ws[cb][tap'][lane][nt] = W[8c + 4cb + lane/16][16nt + lane%16][2-kh'][2-kw'].
-    for (int e = tid; e < CC * CO * 9; e += THREADS) {
-      const int cl = e / (CO * 9), rem = e - cl * (CO * 9);
-      const int o = rem / 9, t = rem - o * 9;
-      const int tapf = 8 - t;  // (2 - kh) * 3 + (2 - kw)
-      const int ln = 16 * (cl & 3) + (o & 15);
-      ws[(((cl >> 2) * 9 + tapf) * 64 + ln) * NT + (o >> 4)] = a.w[((size_t)(CC * c + cl) * CO + o) * 9 + t];
-    }
-    __syncthreads();
-
+    // Next chunk's global loads are in flight while this chunk's MFMAs run.
+    if (c + 1 < NCHUNK) load_chunk<VEC>(a, n, c + 1, h0, w0, tid, r);
 #pragma unroll
     for (int cb = 0; cb < CC / 4; ++cb) {
 #pragma unroll
@@ -126,6 +223,11 @@ __global__ __launch_bounds__(THREADS) void convT2d_pool_htanh_mean_tanh_kernel(C
           acc[mt][3] = mfma16x16x4(av[mt], bv.w, acc[mt][3]);
         }
       }
+    }
+    if (c + 1 < NCHUNK) {
+      __syncthreads();  // every wave is done reading chunk c
+      store_chunk(xs, ws, tid, r);
+      __syncthreads();
     }
   }
 
@@ -193,6 +295,7 @@ __global__ __launch_bounds__(THREADS) void convT2d_pool_htanh_mean_tanh_kernel(C
 }
 
 constexpr size_t kTicketAlign = 256;
+constexpr size_t kWprepBytes = (size_t)NCHUNK * WS_FLOATS * sizeof(float);  // 147,456
 
 void convT_tiles(int H, int W, int *tiles_x, int *tiles_per_image) {
   const int PH = H / 2, PW = W / 2;
@@ -202,11 +305,12 @@ void convT_tiles(int H, int W, int *tiles_x, int *tiles_per_image) {
 
 }  // namespace
 
+// Workspace: [per-image counters, padded to 256 B][prepared weight][partials].
 size_t convT_workspace_bytes(int N, int H, int W) {
   int tx, tpi;
   convT_tiles(H, W, &tx, &tpi);
   const size_t tick = ((size_t)N * sizeof(unsigned) + kTicketAlign - 1) / kTicketAlign * kTicketAlign;
-  return tick + (size_t)N * tpi * 64 * sizeof(float);
+  return tick + kWprepBytes + (size_t)N * tpi * 64 * sizeof(float);
 }
 
 int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b, float *y,
@@ -226,12 +330,23 @@ int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const fl
   a.hi = hi;
   a.inv_count = (float)(1.0 / ((double)a.PH * (double)a.PW));
   const size_t tick = ((size_t)N * sizeof(unsigned) + kTicketAlign - 1) / kTicketAlign * kTicketAlign;
-  a.tickets = reinterpret_cast<unsigned *>(workspace);
-  a.partials = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + tick);
+  char *wsp = reinterpret_cast<char *>(workspace);
+  float *wprep = reinterpret_cast<float *>(wsp + tick);
+  a.tickets = reinterpret_cast<unsigned *>(wsp);
+  a.wprep = wprep;
+  a.partials = reinterpret_cast<float *>(wsp + tick + kWprepBytes);
   const long long grid = (long long)N * a.tiles_per_image;
   if (grid >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
-  hipLaunchKernelGGL(convT2d_pool_htanh_mean_tanh_kernel, dim3((unsigned)grid), dim3(THREADS), 0,
-                     stream, a);
+  hipLaunchKernelGGL(convT_prepare_weight_kernel, dim3(NCHUNK * WS_FLOATS / THREADS), dim3(THREADS),
+                     0, stream, w, wprep);
+  if (launch_status() != CCE_OK) return CCE_ERR_LAUNCH;
+  const bool vec = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL(convT2d_pool_htanh_mean_tanh_kernel<true>, dim3((unsigned)grid), dim3(THREADS),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL(convT2d_pool_htanh_mean_tanh_kernel<false>, dim3((unsigned)grid),
+                       dim3(THREADS), 0, stream, a);
   return launch_status();
 }
 

@@ -113,11 +113,12 @@ def test_convT_validation(lib):
 
 
 def test_convT_workspace_size(lib):
-    # N counters (padded to 256 bytes) + N * tiles * 64 fp32 partial sums, tiles of
-    # 8 x 16 pooling windows.
-    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(16, 64, 256, 256, 64) == 256 + 16 * 128 * 256
-    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(128, 64, 256, 256, 64) == 512 + 128 * 128 * 256
-    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 64, 2, 2, 64) == 256 + 256
+    # N counters (padded to 256 bytes) + the prepared 64x64x3x3 weight + N * tiles * 64
+    # fp32 partial sums, tiles of 8 x 16 pooling windows.
+    wprep = 64 * 64 * 9 * 4
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(16, 64, 256, 256, 64) == 256 + wprep + 16 * 128 * 256
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(128, 64, 256, 256, 64) == 512 + wprep + 128 * 128 * 256
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 64, 2, 2, 64) == 256 + wprep + 256
     assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 64, 16, 16, 64, stride=2) == 0
 
 
