@@ -27,9 +27,94 @@ __device__ __forceinline__ float clampf(float v, float lo, float hi) {
   return fminf(fmaxf(v, lo), hi);
 }
 
+// Division of a non-negative 31-bit integer by a divisor fixed per launch,
+// by multiplication (Granlund & Montgomery, "Division by invariant integers
+// using multiplication", 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l for
+// 0 <= n < 2^31 (the sum cannot overflow because mulhi(n, m) <= n).
+struct FastDiv {
+  uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, l};
+}
+
+__device__ __forceinline__ int fdiv(int n, const FastDiv &f) {
+  const uint32_t t = __umulhi((uint32_t)n, f.m);
+  return (int)((t + (uint32_t)n) >> f.l);
+}
+
 // 16-byte global store of four consecutive floats (address 16-byte aligned).
 __device__ __forceinline__ void store4(float *p, v4f v) {
   *reinterpret_cast<v4f *>(p) = v;
 }
+
+// Stages a tile made of equal-length rows (each `len` floats, contiguous in
+// global memory and in LDS) with a fixed thread -> column assignment, so that
+// a whole tile's global loads can be issued into registers one tile ahead of
+// use and written to LDS later.  VEC moves 16-byte quads (row lengths,
+// sources and destinations four-float aligned), otherwise single floats.
+// Rows beyond KPRE passes, and columns beyond one pass, fall back to
+// synchronous copies in store().
+template <int KPRE, bool VEC, int THREADS>
+struct RowStage {
+  v4f v[KPRE];
+  int cw, tpr, rpp, my_row, my_col;
+
+  __device__ __forceinline__ void init(int len, int tid) {
+    cw = VEC ? (len >> 2) : len;
+    tpr = cw < THREADS ? cw : THREADS;
+    rpp = THREADS / tpr;
+    my_row = tid / tpr;
+    my_col = tid - my_row * tpr;
+  }
+
+  // src(row) -> const float* of the row's first element.
+  template <class Src>
+  __device__ __forceinline__ void load(int rows, Src src) {
+#pragma unroll
+    for (int k = 0; k < KPRE; ++k) {
+      const int row = my_row + k * rpp;
+      if (my_row < rpp && row < rows) {
+        const float *p = src(row);
+        if (VEC)
+          v[k] = *reinterpret_cast<const v4f *>(p + 4 * my_col);
+        else
+          v[k].x = p[my_col];
+      }
+    }
+  }
+
+  // dst(row) -> float* of the row's first element in LDS.
+  template <class Src, class Dst>
+  __device__ __forceinline__ void store(int rows, Src src, Dst dst) {
+#pragma unroll
+    for (int k = 0; k < KPRE; ++k) {
+      const int row = my_row + k * rpp;
+      if (my_row < rpp && row < rows) {
+        float *d = dst(row);
+        if (VEC)
+          *reinterpret_cast<v4f *>(d + 4 * my_col) = v[k];
+        else
+          d[my_col] = v[k].x;
+      }
+    }
+    if (my_row >= rpp) return;
+    for (int row = my_row, k = 0; row < rows; row += rpp, ++k) {
+      const float *p = src(row);
+      float *d = dst(row);
+      for (int c = (k < KPRE ? my_col + tpr : my_col); c < cw; c += tpr) {
+        if (VEC)
+          *reinterpret_cast<v4f *>(d + 4 * c) = *reinterpret_cast<const v4f *>(p + 4 * c);
+        else
+          d[c] = p[c];
+      }
+    }
+  }
+};
 
 }  // namespace cce

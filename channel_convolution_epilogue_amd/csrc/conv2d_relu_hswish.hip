@@ -32,6 +32,7 @@ constexpr int KSTEPS = (CI / 4) * TAPS;  // 18 steps of 4 taps
 constexpr int NT = CO / 16;              // 4 channel blocks of 16
 constexpr int WAVES = 4, THREADS = 64 * WAVES;
 constexpr int MT_BATCH = 2;              // 16-pixel blocks in flight per wave
+constexpr int kPrefetchPasses = 10;      // a 512-pixel tile of 128-wide rows: 80 rows / 8 per pass
 
 struct Conv2dArgs {
   const float *__restrict__ x;
@@ -43,17 +44,49 @@ struct Conv2dArgs {
   int Q;         // output pixels over the batch, N*P
   int ntiles;    // ceil(Q / tile)
   int chstride;  // floats between channel planes in LDS
+  FastDiv divP, divWo, divH;
 };
 
+// HardSwish(ReLU(v)) = r * clamp((r + 3) / 6, 0, 1) with r = max(v, 0).  For
+// v >= 0 the gate (v + 3) / 6 is at least 0.5, and for v < 0 the product is 0
+// whatever the gate, so the gate can be taken from v itself and clamped to
+// [0.5, 1]: four operations.
 __device__ __forceinline__ float relu_hswish(float v) {
-  const float r = fmaxf(v, 0.0f);
-  return r * fminf((r + 3.0f) * (1.0f / 6.0f), 1.0f);
+  const float gate = __builtin_amdgcn_fmed3f(fmaf(v, 1.0f / 6.0f, 0.5f), 0.5f, 1.0f);
+  return fmaxf(v, 0.0f) * gate;
 }
 
+// Input rows of one tile: flat output pixels [q0, q0 + TILE) need input rows
+// r = n * H + h from r_first to r_first + R - 1 of all 8 channels.
+struct TileRows {
+  int q0, r_first, R;
+};
+
+// Staged row `row` = rr * 8 + ci  <->  input row r_first + rr of channel ci.
+struct Conv2dSrc {
+  const float *x;
+  int H, W, r_first;
+  FastDiv divH;
+  __device__ __forceinline__ const float *operator()(int row) const {
+    const int ci = row & (CI - 1), rr = row >> 3;
+    const int r = r_first + rr, n = fdiv(r, divH), hh = r - n * H;
+    return x + (((size_t)n * CI + ci) * H + hh) * W;
+  }
+};
+struct Conv2dDst {
+  float *lds;
+  int chstride, W;
+  __device__ __forceinline__ float *operator()(int row) const {
+    return lds + (row & (CI - 1)) * chstride + (row >> 3) * W;
+  }
+};
+
 // MT_WAVE: 16-pixel blocks per wave per tile (tile = 16 * MT_WAVE * WAVES pixels).
-// VLOAD: W % 4 == 0 (16-byte row loads).  VSTORE: P % 4 == 0 and y 16-byte aligned.
-template <int MT_WAVE, bool VLOAD, bool VSTORE>
-__global__ __launch_bounds__(THREADS) void conv2d_relu_hswish_kernel(Conv2dArgs a) {
+// VLOAD: W % 4 == 0 and x 16-byte aligned (16-byte row loads).
+// VSTORE: P % 4 == 0 and y 16-byte aligned (16-byte result stores).
+// KPRE: staged row passes held in registers while the previous tile computes.
+template <int MT_WAVE, bool VLOAD, bool VSTORE, int KPRE>
+__global__ __launch_bounds__(THREADS, 2) void conv2d_relu_hswish_kernel(Conv2dArgs a) {
   constexpr int TILE = 16 * MT_WAVE * WAVES;
   extern __shared__ float lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -73,40 +106,39 @@ __global__ __launch_bounds__(THREADS) void conv2d_relu_hswish_kernel(Conv2dArgs 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
 
+  // Persistent workgroup: a contiguous run of tiles, so the input rows that
+  // neighbouring tiles share stay in this XCD's L2.
   const int t_begin = (int)(((long long)blockIdx.x * a.ntiles) / gridDim.x);
   const int t_end = (int)(((long long)(blockIdx.x + 1) * a.ntiles) / gridDim.x);
+  if (t_begin >= t_end) return;
+
+  auto rows_of = [&](int t) {
+    TileRows tr;
+    tr.q0 = t * TILE;
+    const int qlast = min(tr.q0 + TILE, a.Q) - 1;
+    const int n0 = fdiv(tr.q0, a.divP), n1 = fdiv(qlast, a.divP);
+    tr.r_first = n0 * a.H + fdiv(tr.q0 - n0 * a.P, a.divWo);
+    tr.R = n1 * a.H + fdiv(qlast - n1 * a.P, a.divWo) + (KS - 1) - tr.r_first + 1;
+    return tr;
+  };
+  auto src_of = [&](const TileRows &tr) { return Conv2dSrc{a.x, a.H, a.W, tr.r_first, a.divH}; };
+  auto dst_of = [&](const TileRows &) { return Conv2dDst{lds, a.chstride, a.W}; };
+
+  RowStage<KPRE, VLOAD, THREADS> stage;
+  stage.init(a.W, tid);
+  TileRows cur = rows_of(t_begin);
+  stage.load(CI * cur.R, src_of(cur));
+  stage.store(CI * cur.R, src_of(cur), dst_of(cur));
+  __syncthreads();
 
   for (int t = t_begin; t < t_end; ++t) {
-    const int q0 = t * TILE;
-    const int qlast = min(q0 + TILE, a.Q) - 1;
-    const int n0 = q0 / a.P, n1 = qlast / a.P;
-    // Input rows are numbered r = n * H + h; the tile needs rows r_first..r_last.
-    const int r_first = n0 * a.H + (q0 - n0 * a.P) / a.Wo;
-    const int r_last = n1 * a.H + (qlast - n1 * a.P) / a.Wo + (KS - 1);
-    const int R = r_last - r_first + 1;
-
-    __syncthreads();  // the previous tile's LDS reads are done
-    {
-      const int cw = VLOAD ? (a.W >> 2) : a.W;  // copy units per row
-      const int tpr = cw < THREADS ? cw : THREADS;
-      const int rpp = THREADS / tpr;
-      const int my_row = tid / tpr, my_col = tid - my_row * tpr;
-      if (my_row < rpp) {
-        for (int ri = my_row; ri < CI * R; ri += rpp) {
-          const int ci = ri / R, rr = ri - ci * R;
-          const int r = r_first + rr, n = r / a.H, hh = r - n * a.H;
-          const float *src = a.x + (((size_t)n * CI + ci) * a.H + hh) * a.W;
-          float *dst = lds + ci * a.chstride + rr * a.W;
-          if (VLOAD) {
-            for (int c = my_col; c < cw; c += tpr)
-              *reinterpret_cast<v4f *>(dst + 4 * c) = *reinterpret_cast<const v4f *>(src + 4 * c);
-          } else {
-            for (int c = my_col; c < cw; c += tpr) dst[c] = src[c];
-          }
-        }
-      }
+    const bool more = t + 1 < t_end;
+    TileRows nxt = cur;
+    if (more) {
+      nxt = rows_of(t + 1);
+      stage.load(CI * nxt.R, src_of(nxt));  // in flight during this tile's MFMAs
     }
-    __syncthreads();
+    const int q0 = cur.q0, r_first = cur.r_first;
 
 #pragma unroll 1
     for (int mb = 0; mb < MT_WAVE; mb += MT_BATCH) {
@@ -115,7 +147,7 @@ __global__ __launch_bounds__(THREADS) void conv2d_relu_hswish_kernel(Conv2dArgs 
       for (int j = 0; j < MT_BATCH; ++j) {
         int q = q0 + 16 * (wave * MT_WAVE + mb + j) + col;
         q = min(q, a.Q - 1);  // lanes past the end read a valid pixel; their results are dropped
-        const int n = q / a.P, p = q - n * a.P, h = p / a.Wo, w = p - h * a.Wo;
+        const int n = fdiv(q, a.divP), p = q - n * a.P, h = fdiv(p, a.divWo), w = p - h * a.Wo;
         base[j] = g * a.chstride + (n * a.H + h - r_first) * a.W + w;
       }
       v4f acc[MT_BATCH][NT];
@@ -143,7 +175,7 @@ __global__ __launch_bounds__(THREADS) void conv2d_relu_hswish_kernel(Conv2dArgs 
         if (qq >= a.Q) continue;
         if (VSTORE) {
           // P % 4 == 0 and Q % 4 == 0: the four pixels are in one plane and all valid.
-          const int n = qq / a.P, p = qq - n * a.P;
+          const int n = fdiv(qq, a.divP), p = qq - n * a.P;
           float *dst = a.y + (size_t)n * CO * a.P + p;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
@@ -159,7 +191,7 @@ __global__ __launch_bounds__(THREADS) void conv2d_relu_hswish_kernel(Conv2dArgs 
           for (int r = 0; r < 4; ++r) {
             const int qr = qq + r;
             if (qr >= a.Q) break;
-            const int n = qr / a.P, p = qr - n * a.P;
+            const int n = fdiv(qr, a.divP), p = qr - n * a.P;
             float *dst = a.y + (size_t)n * CO * a.P + p;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
@@ -167,6 +199,13 @@ __global__ __launch_bounds__(THREADS) void conv2d_relu_hswish_kernel(Conv2dArgs 
           }
         }
       }
+    }
+
+    if (more) {
+      __syncthreads();  // every wave is done reading this tile's rows
+      stage.store(CI * nxt.R, src_of(nxt), dst_of(nxt));
+      __syncthreads();
+      cur = nxt;
     }
   }
 }
@@ -180,7 +219,7 @@ int launch_instance(const Conv2dArgs &a, int R_max, hipStream_t stream) {
   const size_t lds_bytes = (size_t)CI * a.chstride * sizeof(float);
   (void)R_max;
   if (lds_bytes > dev.lds_per_block) return CCE_ERR_UNSUPPORTED;
-  auto kern = conv2d_relu_hswish_kernel<MT_WAVE, VL, VS>;
+  auto kern = conv2d_relu_hswish_kernel<MT_WAVE, VL, VS, kPrefetchPasses>;
   if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds_bytes) != hipSuccess)
     return CCE_ERR_LAUNCH;
@@ -209,6 +248,9 @@ int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, fl
   const int Ho = H - (KS - 1);
   a.P = Ho * a.Wo;
   a.Q = N * a.P;
+  a.divP = make_fastdiv((uint32_t)a.P);
+  a.divWo = make_fastdiv((uint32_t)a.Wo);
+  a.divH = make_fastdiv((uint32_t)H);
 
   DeviceInfo dev;
   if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;

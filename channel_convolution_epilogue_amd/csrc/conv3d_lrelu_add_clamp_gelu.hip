@@ -29,6 +29,7 @@ constexpr int KSTEPS = (CI / 4) * TAPS;  // 54 steps of 4 taps
 constexpr int NTW = 2;                   // 16-channel blocks per wave (32 channels)
 constexpr int WAVES = 4, THREADS = 64 * WAVES;
 constexpr int MT_BATCH = 2;
+constexpr int kPrefetchPasses = 5;  // one plane: 8 ch x 10 rows of 64 floats, 16 rows per pass
 
 struct Conv3dArgs {
   const float *__restrict__ x;
@@ -43,16 +44,72 @@ struct Conv3dArgs {
   int chstride;     // floats between channel blocks in LDS
   int planestride;  // floats between depth planes in LDS, (TR + 2) * W
   float slope, lo, hi;
+  FastDiv divDo, divRowtiles, divWo;
 };
 
+// GELU(t) = 0.5 t (1 + erf(t / sqrt 2)) for |t| <= 1, from the Maclaurin series
+//   erf(z) = (2 / sqrt(pi)) sum_n (-1)^n z^(2n+1) / (n! (2n + 1))
+// (Abramowitz & Stegun 7.1.5).  With u = t^2 and z = t / sqrt 2,
+//   GELU(t) = 0.5 t + u * R(u),   R(u) = sum_n r_n u^n,
+//   r_n = (-1)^n / (sqrt(2 pi) n! (2n + 1) 2^n).
+// The series alternates with decreasing terms for |z| < 1, so stopping after
+// n = 7 errs by less than the n = 8 term: 2/sqrt(pi) z^17 / (8! 17) < 5e-9 at
+// |z| = 1/sqrt 2 -- below fp32 rounding of the result.
+constexpr double gelu_series_coef(int n) {
+  double c = 0.3989422804014327;  // 1 / sqrt(2 pi)
+  for (int k = 1; k <= n; ++k) c *= -1.0 / (2.0 * k);
+  return c / (2 * n + 1);
+}
+__device__ __forceinline__ float gelu_small(float t) {
+  const float u = t * t;
+  float r = (float)gelu_series_coef(7);
+  r = fmaf(r, u, (float)gelu_series_coef(6));
+  r = fmaf(r, u, (float)gelu_series_coef(5));
+  r = fmaf(r, u, (float)gelu_series_coef(4));
+  r = fmaf(r, u, (float)gelu_series_coef(3));
+  r = fmaf(r, u, (float)gelu_series_coef(2));
+  r = fmaf(r, u, (float)gelu_series_coef(1));
+  r = fmaf(r, u, (float)gelu_series_coef(0));
+  return fmaf(u, r, 0.5f * t);
+}
+
+// LeakyReLU -> + s -> clamp -> GELU.  SERIES: the clamp bounds lie in [-1, 1],
+// so the series above applies; otherwise the device library's erff.
+template <bool SERIES>
 __device__ __forceinline__ float epilogue(float v, float s, float slope, float lo, float hi) {
   float t = v >= 0.0f ? v : slope * v;
   t = clampf(t + s, lo, hi);
+  if (SERIES) return gelu_small(t);
   return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
 }
 
-template <bool VLOAD, bool VSTORE>
-__global__ __launch_bounds__(THREADS) void conv3d_lrelu_add_clamp_gelu_kernel(Conv3dArgs a) {
+// One tile: output depth plane d of image n, output rows h0 .. h0 + rows - 1.
+// Tiles are numbered with d fastest, so a run of consecutive tiles walks down
+// the depth axis of one row block and each step needs one new input plane.
+struct Tile3 {
+  int n, d, h0, rows;
+};
+
+// One input depth plane dd of a row block: staged row `row` = rr * 8 + ci
+// <-> x[n][ci][dd][h0 + rr][:], stored in LDS ring slot dd % 3.
+struct PlaneSrc {
+  const float *x;
+  int D, H, W, n, dd, h0;
+  __device__ __forceinline__ const float *operator()(int row) const {
+    const int ci = row & (CI - 1), rr = row >> 3;
+    return x + ((((size_t)n * CI + ci) * D + dd) * H + (h0 + rr)) * W;
+  }
+};
+struct PlaneDst {
+  float *lds;
+  int chstride, slot_off, W;
+  __device__ __forceinline__ float *operator()(int row) const {
+    return lds + (row & (CI - 1)) * chstride + slot_off + (row >> 3) * W;
+  }
+};
+
+template <bool VLOAD, bool VSTORE, bool SERIES, int KPRE>
+__global__ __launch_bounds__(THREADS, 2) void conv3d_lrelu_add_clamp_gelu_kernel(Conv3dArgs a) {
   extern __shared__ float lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -78,50 +135,68 @@ __global__ __launch_bounds__(THREADS) void conv3d_lrelu_add_clamp_gelu_kernel(Co
 
   const int t_begin = (int)(((long long)blockIdx.x * a.ntiles) / gridDim.x);
   const int t_end = (int)(((long long)(blockIdx.x + 1) * a.ntiles) / gridDim.x);
+  if (t_begin >= t_end) return;
+
+  auto tile_of = [&](int t) {
+    Tile3 tl;
+    const int q = fdiv(t, a.divDo);
+    tl.d = t - q * a.Do;
+    tl.n = fdiv(q, a.divRowtiles);
+    const int rt = q - tl.n * a.rowtiles;
+    tl.h0 = rt * a.TR;
+    tl.rows = min(a.TR, a.Ho - tl.h0);
+    return tl;
+  };
+  auto src_of = [&](const Tile3 &tl, int dd) {
+    return PlaneSrc{a.x, a.D, a.H, a.W, tl.n, dd, tl.h0};
+  };
+  auto dst_of = [&](const Tile3 &, int dd) {
+    return PlaneDst{lds, a.chstride, (dd % KS) * a.planestride, a.W};
+  };
+  auto nrows = [&](const Tile3 &tl) { return CI * (tl.rows + (KS - 1)); };
+
+  // Registers carry one input plane ahead: plane d + 3 while tile d computes,
+  // or the first plane of a new row block (its other two are copied directly).
+  RowStage<KPRE, VLOAD, THREADS> stage;
+  stage.init(a.W, tid);
+  Tile3 cur = tile_of(t_begin);
+  stage.load(nrows(cur), src_of(cur, cur.d));
+  stage.store(nrows(cur), src_of(cur, cur.d), dst_of(cur, cur.d));
+  stage.load(nrows(cur), src_of(cur, cur.d + 1));
+  stage.store(nrows(cur), src_of(cur, cur.d + 1), dst_of(cur, cur.d + 1));
+  stage.load(nrows(cur), src_of(cur, cur.d + 2));
+  stage.store(nrows(cur), src_of(cur, cur.d + 2), dst_of(cur, cur.d + 2));
+  __syncthreads();
 
   for (int t = t_begin; t < t_end; ++t) {
-    const int rt = t % a.rowtiles, nd = t / a.rowtiles;
-    const int d = nd % a.Do, n = nd / a.Do;
-    const int h0 = rt * a.TR;
-    const int rows = min(a.TR, a.Ho - h0);
-    const int V = rows * a.Wo;  // voxels in this tile
-    const int MTT = (V + 15) >> 4;
-    const int rows_in = rows + (KS - 1);
-
-    __syncthreads();
-    {
-      const int cw = VLOAD ? (a.W >> 2) : a.W;
-      const int tpr = cw < THREADS ? cw : THREADS;
-      const int rpp = THREADS / tpr;
-      const int my_row = tid / tpr, my_col = tid - my_row * tpr;
-      const int nrows = CI * KS * rows_in;
-      if (my_row < rpp) {
-        for (int ri = my_row; ri < nrows; ri += rpp) {
-          const int rr = ri % rows_in, pk = ri / rows_in, kd = pk % KS, ci = pk / KS;
-          const float *src =
-              a.x + ((((size_t)n * CI + ci) * a.D + (d + kd)) * a.H + (h0 + rr)) * a.W;
-          float *dst = lds + ci * a.chstride + kd * a.planestride + rr * a.W;
-          if (VLOAD) {
-            for (int c = my_col; c < cw; c += tpr)
-              *reinterpret_cast<v4f *>(dst + 4 * c) = *reinterpret_cast<const v4f *>(src + 4 * c);
-          } else {
-            for (int c = my_col; c < cw; c += tpr) dst[c] = src[c];
-          }
-        }
-      }
+    const bool more = t + 1 < t_end;
+    Tile3 nxt = cur;
+    bool fresh = false;  // next tile starts a new row block (needs three planes)
+    if (more) {
+      nxt = tile_of(t + 1);
+      fresh = nxt.d == 0;
+      stage.load(nrows(nxt), src_of(nxt, fresh ? 0 : nxt.d + 2));
     }
-    __syncthreads();
-
-    float *ybase = a.y + ((size_t)n * CO) * vol + (size_t)d * a.Ho * a.Wo + (size_t)h0 * a.Wo;
+    const int V = cur.rows * a.Wo;  // voxels in this tile
+    const int MTT = (V + 15) >> 4;
+    float *ybase = a.y + ((size_t)cur.n * CO) * vol + (size_t)cur.d * a.Ho * a.Wo +
+                   (size_t)cur.h0 * a.Wo;
+    // LDS offsets of input planes d, d + 1, d + 2 in the ring.
+    const int so0 = (cur.d % KS) * a.planestride;
+    const int so1 = ((cur.d + 1) % KS) * a.planestride;
+    const int so2 = ((cur.d + 2) % KS) * a.planestride;
 
 #pragma unroll 1
     for (int mb = mg * MT_BATCH; mb < MTT; mb += 2 * MT_BATCH) {
-      int base[MT_BATCH];
+      int base[MT_BATCH][KS];
 #pragma unroll
       for (int j = 0; j < MT_BATCH; ++j) {
         const int v = min(16 * (mb + j) + col, V - 1);
-        const int hl = v / a.Wo, w = v - hl * a.Wo;
-        base[j] = g * a.chstride + hl * a.W + w;
+        const int hl = fdiv(v, a.divWo), w = v - hl * a.Wo;
+        const int b0 = g * a.chstride + hl * a.W + w;
+        base[j][0] = b0 + so0;
+        base[j][1] = b0 + so1;
+        base[j][2] = b0 + so2;
       }
       v4f acc[MT_BATCH][NTW];
 #pragma unroll
@@ -132,10 +207,10 @@ __global__ __launch_bounds__(THREADS) void conv3d_lrelu_add_clamp_gelu_kernel(Co
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         const int tt = s % TAPS, kd = tt / 9, kh = (tt / 3) % 3, kw = tt % 3;
-        const int off = (s / TAPS) * 4 * a.chstride + kd * a.planestride + kh * a.W + kw;
+        const int off = (s / TAPS) * 4 * a.chstride + kh * a.W + kw;
         float av[MT_BATCH];
 #pragma unroll
-        for (int j = 0; j < MT_BATCH; ++j) av[j] = lds[base[j] + off];
+        for (int j = 0; j < MT_BATCH; ++j) av[j] = lds[base[j][kd] + off];
 #pragma unroll
         for (int j = 0; j < MT_BATCH; ++j)
 #pragma unroll
@@ -151,10 +226,10 @@ __global__ __launch_bounds__(THREADS) void conv3d_lrelu_add_clamp_gelu_kernel(Co
           const int o = 32 * half + 16 * nt + col;
           float *dst = ybase + (size_t)o * vol + v0;
           v4f r = acc[j][nt];
-          r.x = epilogue(r.x, sadd[nt], a.slope, a.lo, a.hi);
-          r.y = epilogue(r.y, sadd[nt], a.slope, a.lo, a.hi);
-          r.z = epilogue(r.z, sadd[nt], a.slope, a.lo, a.hi);
-          r.w = epilogue(r.w, sadd[nt], a.slope, a.lo, a.hi);
+          r.x = epilogue<SERIES>(r.x, sadd[nt], a.slope, a.lo, a.hi);
+          r.y = epilogue<SERIES>(r.y, sadd[nt], a.slope, a.lo, a.hi);
+          r.z = epilogue<SERIES>(r.z, sadd[nt], a.slope, a.lo, a.hi);
+          r.w = epilogue<SERIES>(r.w, sadd[nt], a.slope, a.lo, a.hi);
           if (VSTORE && v0 + 3 < V) {
             store4(dst, r);
           } else {
@@ -166,13 +241,28 @@ __global__ __launch_bounds__(THREADS) void conv3d_lrelu_add_clamp_gelu_kernel(Co
         }
       }
     }
+
+    if (more) {
+      __syncthreads();  // every wave is done reading plane d (its slot is reused)
+      if (fresh) {
+        stage.store(nrows(nxt), src_of(nxt, 0), dst_of(nxt, 0));
+        stage.load(nrows(nxt), src_of(nxt, 1));
+        stage.store(nrows(nxt), src_of(nxt, 1), dst_of(nxt, 1));
+        stage.load(nrows(nxt), src_of(nxt, 2));
+        stage.store(nrows(nxt), src_of(nxt, 2), dst_of(nxt, 2));
+      } else {
+        stage.store(nrows(nxt), src_of(nxt, nxt.d + 2), dst_of(nxt, nxt.d + 2));
+      }
+      __syncthreads();
+      cur = nxt;
+    }
   }
 }
 
-template <bool VL, bool VS>
+template <bool VL, bool VS, bool SER>
 int launch_instance(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev,
                     hipStream_t stream) {
-  auto kern = conv3d_lrelu_add_clamp_gelu_kernel<VL, VS>;
+  auto kern = conv3d_lrelu_add_clamp_gelu_kernel<VL, VS, SER, kPrefetchPasses>;
   if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds_bytes) != hipSuccess)
     return CCE_ERR_LAUNCH;
@@ -184,6 +274,14 @@ int launch_instance(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev
   if (grid > a.ntiles) grid = a.ntiles;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds_bytes, stream, a);
   return launch_status();
+}
+
+template <bool VL, bool VS>
+int launch_series(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev,
+                  hipStream_t stream) {
+  const bool series = a.lo >= -1.0f && a.hi <= 1.0f;
+  return series ? launch_instance<VL, VS, true>(a, lds_bytes, dev, stream)
+                : launch_instance<VL, VS, false>(a, lds_bytes, dev, stream);
 }
 
 }  // namespace
@@ -228,13 +326,16 @@ int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const flo
   const long long nt = (long long)N * a.Do * a.rowtiles;
   if (nt >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
   a.ntiles = (int)nt;
+  a.divDo = make_fastdiv((uint32_t)a.Do);
+  a.divRowtiles = make_fastdiv((uint32_t)a.rowtiles);
+  a.divWo = make_fastdiv((uint32_t)a.Wo);
 
   const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
   const bool vs = ((a.Ho * a.Wo) % 4 == 0) && ((a.TR * a.Wo) % 4 == 0) && ((uintptr_t)y % 16 == 0);
-  if (vl) return vs ? launch_instance<true, true>(a, lds_bytes, dev, stream)
-                    : launch_instance<true, false>(a, lds_bytes, dev, stream);
-  return vs ? launch_instance<false, true>(a, lds_bytes, dev, stream)
-            : launch_instance<false, false>(a, lds_bytes, dev, stream);
+  if (vl) return vs ? launch_series<true, true>(a, lds_bytes, dev, stream)
+                    : launch_series<true, false>(a, lds_bytes, dev, stream);
+  return vs ? launch_series<false, true>(a, lds_bytes, dev, stream)
+            : launch_series<false, false>(a, lds_bytes, dev, stream);
 }
 
 }  // namespace cce
