@@ -30,9 +30,10 @@ namespace {
 constexpr int CI = 8, CO = 64, KS = 3, TAPS = KS * KS;
 constexpr int KSTEPS = (CI / 4) * TAPS;  // 18 steps of 4 taps
 constexpr int NT = CO / 16;              // 4 channel blocks of 16
-constexpr int WAVES = 4, THREADS = 64 * WAVES;
+constexpr int WAVES = 8, THREADS = 64 * WAVES;
 constexpr int MT_BATCH = 2;              // 16-pixel blocks in flight per wave
-constexpr int kPrefetchPasses = 10;      // a 512-pixel tile of 128-wide rows: 80 rows / 8 per pass
+constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // weights in LDS, B-operand order (18 KB)
+constexpr int kPrefetchPasses = 4;       // 64 of a 1024-pixel tile's <= 112 staged rows (16 per pass); the rest load at store time
 
 struct Conv2dArgs {
   const float *__restrict__ x;
@@ -86,31 +87,33 @@ struct Conv2dDst {
 // VSTORE: P % 4 == 0 and y 16-byte aligned (16-byte result stores).
 // KPRE: staged row passes held in registers while the previous tile computes.
 template <int MT_WAVE, bool VLOAD, bool VSTORE, int KPRE>
-__global__ __launch_bounds__(THREADS, 2) void conv2d_relu_hswish_kernel(Conv2dArgs a) {
+__global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dArgs a) {
   constexpr int TILE = 16 * MT_WAVE * WAVES;
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  float *ws = lds;              // weights in B-operand order, WS_FLOATS
+  float *xs = lds + WS_FLOATS;  // input rows, 8 channel planes of chstride floats
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
 
-  // B operand for every K-step and channel block: B[k][n] = w[o][ci][kh][kw]
-  // with o = 16 nt + col, ci = 4 * half + g, step = (half, kh, kw).
-  float wr[KSTEPS][NT];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int o = 16 * nt + col, ci = 4 * (s / TAPS) + g;
-      wr[s][nt] = a.w[(o * CI + ci) * TAPS + (s % TAPS)];
-    }
+  // B operand of K-step s = (half, kh, kw) for all four 16-channel blocks:
+  // ws[s][lane][nt] = w[16 nt + lane % 16][4 half + lane / 16][kh][kw].
+  for (int e = tid; e < WS_FLOATS; e += THREADS) {
+    const int nt = e & 3, ln = (e >> 2) & 63, st = e >> 8;
+    const int o = 16 * nt + (ln & 15), ci = 4 * (st / TAPS) + (ln >> 4);
+    ws[e] = a.w[(o * CI + ci) * TAPS + (st % TAPS)];
+  }
   float bias[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
 
-  // Persistent workgroup: a contiguous run of tiles, so the input rows that
-  // neighbouring tiles share stay in this XCD's L2.
-  const int t_begin = (int)(((long long)blockIdx.x * a.ntiles) / gridDim.x);
-  const int t_end = (int)(((long long)(blockIdx.x + 1) * a.ntiles) / gridDim.x);
-  if (t_begin >= t_end) return;
+  // Tiles are dealt round-robin, so the workgroups running at any moment
+  // write neighbouring stretches of the same output channel planes.  The
+  // hardware hands workgroups to the 8 XCDs in turn (b -> XCD b % 8); the
+  // remap gives each XCD a contiguous block of each round's tiles, so one
+  // L2 collects long runs of every plane.  (gridDim.x is a multiple of 8.)
+  const int per_xcd = gridDim.x >> 3;
+  const int t_begin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3), t_step = gridDim.x;
+  if (t_begin >= a.ntiles) return;
 
   auto rows_of = [&](int t) {
     TileRows tr;
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv2d_relu_hswish_kernel(Conv2dAr
     return tr;
   };
   auto src_of = [&](const TileRows &tr) { return Conv2dSrc{a.x, a.H, a.W, tr.r_first, a.divH}; };
-  auto dst_of = [&](const TileRows &) { return Conv2dDst{lds, a.chstride, a.W}; };
+  auto dst_of = [&](const TileRows &) { return Conv2dDst{xs, a.chstride, a.W}; };
 
   RowStage<KPRE, VLOAD, THREADS> stage;
   stage.init(a.W, tid);
@@ -131,21 +134,27 @@ __global__ __launch_bounds__(THREADS, 2) void conv2d_relu_hswish_kernel(Conv2dAr
   stage.store(CI * cur.R, src_of(cur), dst_of(cur));
   __syncthreads();
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const bool more = t + 1 < t_end;
+  for (int t = t_begin; t < a.ntiles; t += t_step) {
+    const bool more = t + t_step < a.ntiles;
     TileRows nxt = cur;
     if (more) {
-      nxt = rows_of(t + 1);
+      nxt = rows_of(t + t_step);
       stage.load(CI * nxt.R, src_of(nxt));  // in flight during this tile's MFMAs
     }
     const int q0 = cur.q0, r_first = cur.r_first;
 
 #pragma unroll 1
     for (int mb = 0; mb < MT_WAVE; mb += MT_BATCH) {
+      // Compiler-only fence: keeps the per-step weight reads inside the loop
+      // instead of hoisting all 18 of them (72 VGPRs) out of it.
+      asm volatile("" ::: "memory");
+      // The waves' blocks interleave: together they cover one contiguous run
+      // of 16 * MT_BATCH * WAVES pixels per round.
+      const int blk0 = (mb / MT_BATCH * WAVES + wave) * MT_BATCH;
       int base[MT_BATCH];
 #pragma unroll
       for (int j = 0; j < MT_BATCH; ++j) {
-        int q = q0 + 16 * (wave * MT_WAVE + mb + j) + col;
+        int q = q0 + 16 * (blk0 + j) + col;
         q = min(q, a.Q - 1);  // lanes past the end read a valid pixel; their results are dropped
         const int n = fdiv(q, a.divP), p = q - n * a.P, h = fdiv(p, a.divWo), w = p - h * a.Wo;
         base[j] = g * a.chstride + (n * a.H + h - r_first) * a.W + w;
@@ -160,18 +169,22 @@ __global__ __launch_bounds__(THREADS, 2) void conv2d_relu_hswish_kernel(Conv2dAr
       for (int s = 0; s < KSTEPS; ++s) {
         const int tap = s % TAPS;
         const int off = (s / TAPS) * 4 * a.chstride + (tap / KS) * a.W + (tap % KS);
+        const v4f bv = *reinterpret_cast<const v4f *>(&ws[(s * 64 + lane) * NT]);
         float av[MT_BATCH];
 #pragma unroll
-        for (int j = 0; j < MT_BATCH; ++j) av[j] = lds[base[j] + off];
+        for (int j = 0; j < MT_BATCH; ++j) av[j] = xs[base[j] + off];
 #pragma unroll
-        for (int j = 0; j < MT_BATCH; ++j)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[j][nt] = mfma16x16x4(av[j], wr[s][nt], acc[j][nt]);
+        for (int j = 0; j < MT_BATCH; ++j) {
+          acc[j][0] = mfma16x16x4(av[j], bv.x, acc[j][0]);
+          acc[j][1] = mfma16x16x4(av[j], bv.y, acc[j][1]);
+          acc[j][2] = mfma16x16x4(av[j], bv.z, acc[j][2]);
+          acc[j][3] = mfma16x16x4(av[j], bv.w, acc[j][3]);
+        }
       }
 
 #pragma unroll
       for (int j = 0; j < MT_BATCH; ++j) {
-        const int qq = q0 + 16 * (wave * MT_WAVE + mb + j) + 4 * g;  // this lane's first pixel
+        const int qq = q0 + 16 * (blk0 + j) + 4 * g;  // this lane's first pixel
         if (qq >= a.Q) continue;
         if (VSTORE) {
           // P % 4 == 0 and Q % 4 == 0: the four pixels are in one plane and all valid.
@@ -216,7 +229,7 @@ int launch_instance(const Conv2dArgs &a, int R_max, hipStream_t stream) {
   (void)TILE;
   DeviceInfo dev;
   if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
-  const size_t lds_bytes = (size_t)CI * a.chstride * sizeof(float);
+  const size_t lds_bytes = ((size_t)WS_FLOATS + (size_t)CI * a.chstride) * sizeof(float);
   (void)R_max;
   if (lds_bytes > dev.lds_per_block) return CCE_ERR_UNSUPPORTED;
   auto kern = conv2d_relu_hswish_kernel<MT_WAVE, VL, VS, kPrefetchPasses>;
@@ -229,6 +242,7 @@ int launch_instance(const Conv2dArgs &a, int R_max, hipStream_t stream) {
     per_cu = 1;
   int grid = dev.num_cus * per_cu;
   if (grid > a.ntiles) grid = a.ntiles;
+  grid = (grid + 7) & ~7;  // the XCD remap needs a multiple of 8; surplus workgroups exit
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds_bytes, stream, a);
   return launch_status();
 }
@@ -254,9 +268,10 @@ int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, fl
 
   DeviceInfo dev;
   if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
-  // Small problems use 128-pixel tiles so that every CU gets work.
-  const bool small = (a.Q + 511) / 512 < 2 * dev.num_cus;
-  const int tile = small ? 128 : 512;
+  // Tiles of 1024 pixels (8 waves x 8 blocks of 16); small problems use
+  // 256-pixel tiles so that every CU gets work.
+  const bool small = (a.Q + 1023) / 1024 < 2 * dev.num_cus;
+  const int tile = small ? 256 : 1024;
   a.ntiles = (a.Q + tile - 1) / tile;
 
   // Upper bound on the input rows one tile touches: output rows spanned plus

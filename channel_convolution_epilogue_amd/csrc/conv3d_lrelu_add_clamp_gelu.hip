@@ -11,11 +11,12 @@
 //    input -- 8 channels x 3 depth planes x (TR + 2) rows x W -- is staged in
 //    LDS once.  Voxels inside the tile are numbered flat (row-major), so a
 //    lane's four result voxels are consecutive in memory.
-//  * Each wave owns 32 of the 64 output channels; the matching 216 x 32
-//    weight slice lives in 108 VGPRs per lane for the whole (persistent)
-//    workgroup.  Two waves share a channel half and split the tile's
-//    16-voxel blocks.  Per K-step a lane reads one A value from LDS at a
-//    lane-independent step offset (lane group g = channel within a group of 4).
+//  * Each of the 8 waves owns 16 of the 64 output channels; the matching
+//    216 x 16 weight slice lives in 54 VGPRs per lane for the whole
+//    (persistent) workgroup, which keeps 4 waves per SIMD resident.  The
+//    four waves of a channel split the tile's 16-voxel blocks two ways.  Per
+//    K-step a lane reads one A value from LDS at a lane-independent step
+//    offset (lane group g = input channel within a group of 4).
 //  * The epilogue (bias as accumulator init, LeakyReLU, add, clamp, GELU with
 //    erf) runs in registers; only the final value is stored.
 #include "cce_device.hpp"
@@ -26,10 +27,11 @@ namespace {
 
 constexpr int CI = 8, CO = 64, KS = 3, TAPS = KS * KS * KS;
 constexpr int KSTEPS = (CI / 4) * TAPS;  // 54 steps of 4 taps
-constexpr int NTW = 2;                   // 16-channel blocks per wave (32 channels)
-constexpr int WAVES = 4, THREADS = 64 * WAVES;
+constexpr int CG = 4;                    // channel groups of 16: wave w owns channels 16 (w % 4) ..
+constexpr int MG = 2;                    // voxel groups: wave w takes 16-voxel blocks w / 4, + 2, ...
+constexpr int WAVES = CG * MG, THREADS = 64 * WAVES;
 constexpr int MT_BATCH = 2;
-constexpr int kPrefetchPasses = 5;  // one plane: 8 ch x 10 rows of 64 floats, 16 rows per pass
+constexpr int kPrefetchPasses = 3;  // one plane: 8 ch x 10 rows of 64 floats, 32 rows per pass
 
 struct Conv3dArgs {
   const float *__restrict__ x;
@@ -109,28 +111,19 @@ struct PlaneDst {
 };
 
 template <bool VLOAD, bool VSTORE, bool SERIES, int KPRE>
-__global__ __launch_bounds__(THREADS, 2) void conv3d_lrelu_add_clamp_gelu_kernel(Conv3dArgs a) {
+__global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel(Conv3dArgs a) {
   extern __shared__ float lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
-  const int half = wave & 1;  // which 32 output channels
-  const int mg = wave >> 1;   // which interleaved set of 16-voxel blocks
+  const int o = 16 * (wave % CG) + col;  // this lane's output channel
+  const int mg = wave / CG;              // which interleaved set of 16-voxel blocks
 
-  float wr[KSTEPS][NTW];
+  // B operand of every K-step for this wave's 16 channels (54 VGPRs).
+  float wr[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const int o = 32 * half + 16 * nt + col, ci = 4 * (s / TAPS) + g;
-      wr[s][nt] = a.w[(o * CI + ci) * TAPS + (s % TAPS)];
-    }
-  float bias[NTW], sadd[NTW];
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const int o = 32 * half + 16 * nt + col;
-    bias[nt] = a.b ? a.b[o] : 0.0f;
-    sadd[nt] = a.s[o];
-  }
+  for (int s = 0; s < KSTEPS; ++s) wr[s] = a.w[(o * CI + 4 * (s / TAPS) + g) * TAPS + (s % TAPS)];
+  const float bias = a.b ? a.b[o] : 0.0f;
+  const float sadd = a.s[o];
   const size_t vol = (size_t)a.Do * a.Ho * a.Wo;  // output voxels per (n, channel)
 
   const int t_begin = (int)(((long long)blockIdx.x * a.ntiles) / gridDim.x);
@@ -187,7 +180,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3d_lrelu_add_clamp_gelu_kernel
     const int so2 = ((cur.d + 2) % KS) * a.planestride;
 
 #pragma unroll 1
-    for (int mb = mg * MT_BATCH; mb < MTT; mb += 2 * MT_BATCH) {
+    for (int mb = mg * MT_BATCH; mb < MTT; mb += MG * MT_BATCH) {
       int base[MT_BATCH][KS];
 #pragma unroll
       for (int j = 0; j < MT_BATCH; ++j) {
@@ -198,11 +191,9 @@ __global__ __launch_bounds__(THREADS, 2) void conv3d_lrelu_add_clamp_gelu_kernel
         base[j][1] = b0 + so1;
         base[j][2] = b0 + so2;
       }
-      v4f acc[MT_BATCH][NTW];
+      v4f acc[MT_BATCH];
 #pragma unroll
-      for (int j = 0; j < MT_BATCH; ++j)
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) acc[j][nt] = splat4(bias[nt]);
+      for (int j = 0; j < MT_BATCH; ++j) acc[j] = splat4(bias);
 
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
@@ -212,32 +203,26 @@ __global__ __launch_bounds__(THREADS, 2) void conv3d_lrelu_add_clamp_gelu_kernel
 #pragma unroll
         for (int j = 0; j < MT_BATCH; ++j) av[j] = lds[base[j][kd] + off];
 #pragma unroll
-        for (int j = 0; j < MT_BATCH; ++j)
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt) acc[j][nt] = mfma16x16x4(av[j], wr[s][nt], acc[j][nt]);
+        for (int j = 0; j < MT_BATCH; ++j) acc[j] = mfma16x16x4(av[j], wr[s], acc[j]);
       }
 
 #pragma unroll
       for (int j = 0; j < MT_BATCH; ++j) {
         const int v0 = 16 * (mb + j) + 4 * g;
         if (v0 >= V) continue;
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          const int o = 32 * half + 16 * nt + col;
-          float *dst = ybase + (size_t)o * vol + v0;
-          v4f r = acc[j][nt];
-          r.x = epilogue<SERIES>(r.x, sadd[nt], a.slope, a.lo, a.hi);
-          r.y = epilogue<SERIES>(r.y, sadd[nt], a.slope, a.lo, a.hi);
-          r.z = epilogue<SERIES>(r.z, sadd[nt], a.slope, a.lo, a.hi);
-          r.w = epilogue<SERIES>(r.w, sadd[nt], a.slope, a.lo, a.hi);
-          if (VSTORE && v0 + 3 < V) {
-            store4(dst, r);
-          } else {
-            dst[0] = r.x;
-            if (v0 + 1 < V) dst[1] = r.y;
-            if (v0 + 2 < V) dst[2] = r.z;
-            if (v0 + 3 < V) dst[3] = r.w;
-          }
+        float *dst = ybase + (size_t)o * vol + v0;
+        v4f r = acc[j];
+        r.x = epilogue<SERIES>(r.x, sadd, a.slope, a.lo, a.hi);
+        r.y = epilogue<SERIES>(r.y, sadd, a.slope, a.lo, a.hi);
+        r.z = epilogue<SERIES>(r.z, sadd, a.slope, a.lo, a.hi);
+        r.w = epilogue<SERIES>(r.w, sadd, a.slope, a.lo, a.hi);
+        if (VSTORE && v0 + 3 < V) {
+          store4(dst, r);
+        } else {
+          dst[0] = r.x;
+          if (v0 + 1 < V) dst[1] = r.y;
+          if (v0 + 2 < V) dst[2] = r.z;
+          if (v0 + 3 < V) dst[3] = r.w;
         }
       }
     }
