@@ -1,13 +1,14 @@
 """Benchmark of the fused small-channel convolution + epilogue kernels on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--ops all|none]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm S] [--workload NAME] [--ops all|none]
                     [--no-cpu-baseline] [--seed S]
 
 One step is one call of the headline workload's fused operator on one batch
 of seeded synthetic input already resident in device memory (the default
 headline is Conv2d 3x3 8->64 + ReLU + HardSwish at N = 128, 128 x 128).
-W untimed warm-up steps, then exactly K timed steps bracketed by device
-synchronisations; HIP events on the stream the kernels run on give the
+S seconds of untimed pre-warm calls (an idle GPU needs a moment of load
+before its clocks settle), W untimed warm-up steps, then exactly K timed
+steps bracketed by device synchronisations; HIP events on the stream the kernels run on give the
 per-launch kernel time.  Rank 0 prints one JSON line with the headline
 throughput (GFLOP/s of the convolution's multiply-adds, 2 FLOP each), the
 roofline of the dominant kernel, the CPU oracle's throughput on a bounded
@@ -88,6 +89,66 @@ def measured_traffic(op: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+DOMINANT_KERNEL = {  # substring of the kernel symbol that dominates each operator's time
+    CONV2D: "conv2d_relu_hswish_kernel",
+    CONV3D: "conv3d_lrelu_add_clamp_gelu_kernel",
+    CONVT: "convT2d_pool_htanh_mean_tanh_kernel",
+}
+COPY_KERNEL = "copyBuffer"  # torch's device-to-device copy under ROCm
+
+
+def _counter_per_dispatch(csv_path: Path, kernel_substr: str, counter: str):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    return (sum(vals) / len(vals)) if vals else None
+
+
+def record_traffic(pmc_dir: Path, copy_mib: int) -> dict:
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) into HBM
+    bytes per launch of each workload's dominant kernel.  Each counter is
+    scaled by the factor that makes it read exactly `copy_mib` MiB for a plain
+    device copy of that size.  Expects <dir>/{fetch,write}_<workload>/ and
+    <dir>/{fetch,write}_copy/ from `rocprofv3 --pmc ... --output-format csv -o run`."""
+    known = copy_mib * 1024 * 1024
+    scale = {}
+    for kind, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        kib = _counter_per_dispatch(pmc_dir / f"{kind}_copy" / "run_counter_collection.csv",
+                                    COPY_KERNEL, counter)
+        scale[kind] = known / (kib * 1024.0)
+    out = {"_about": ("HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                      "dispatch), each scaled so that a plain %d MiB device copy reads/writes "
+                      "exactly %d MiB; valid while the kernel source digest matches." % (copy_mib, copy_mib)),
+           "copy_scale": {k: round(v, 5) for k, v in scale.items()}}
+    for name, cfg in WORKLOADS.items():
+        op = cfg["op"]
+        f = pmc_dir / f"fetch_{name}" / "run_counter_collection.csv"
+        w = pmc_dir / f"write_{name}" / "run_counter_collection.csv"
+        if not (f.exists() and w.exists()):
+            continue
+        fk = _counter_per_dispatch(f, DOMINANT_KERNEL[op], "FETCH_SIZE")
+        wk = _counter_per_dispatch(w, DOMINANT_KERNEL[op], "WRITE_SIZE")
+        fb, wb = fk * 1024 * scale["fetch"], wk * 1024 * scale["write"]
+        out[name] = {"kernel": DOMINANT_KERNEL[op], "source_sha256_16": source_digest(op),
+                     "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+                     "bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb), "write_bytes": int(wb),
+                     "algorithmic_bytes": work_counts(dict(cfg))["bytes"]}
+    return out
+
+
+def copy_probe(mib: int, reps: int) -> None:
+    """A plain device-to-device copy of `mib` MiB, `reps` times: the known-size
+    reference that calibrates the HBM byte counters."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    a = torch.empty(n, device="cuda")
+    b = torch.ones(n, device="cuda")
+    for _ in range(reps):
+        a.copy_(b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_mib": mib, "reps": reps}))
+
+
 def run_op(cce, shape, d):
     op = shape["op"]
     if op == CONV2D:
@@ -115,11 +176,18 @@ def device_inputs(torch, cce, shape, p):
     return d
 
 
-def time_workload(torch, cce, name, steps, warmup, seed):
+def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0):
     shape, p = workload_inputs(name, seed)
     d = device_inputs(torch, cce, shape, p)
     del p
     fn = run_op(cce, shape, d)
+    # Bring the GPU out of its idle clocks first: a freshly idle MI355X needs a
+    # fraction of a second of load before kernel times settle.
+    t_end = time.perf_counter() + prewarm_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -199,14 +267,29 @@ def cpu_baseline(name, seed, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser(description="fused conv + epilogue benchmark (one MI355X)")
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prewarm", type=float, default=1.0,
+                    help="seconds of untimed calls before the warm-up steps (GPU clock ramp)")
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--ops", default="all", choices=["all", "none"],
                     help="also time every other fused workload (reported under 'ops')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-probe", type=int, metavar="MIB",
+                    help="only run a plain MIB-MiB device copy (counter calibration) and exit")
+    ap.add_argument("--record-traffic", metavar="PMC_DIR",
+                    help="only convert rocprofv3 FETCH_SIZE/WRITE_SIZE runs in PMC_DIR into "
+                         "profiles/hbm_traffic.json and exit")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        rec = record_traffic(Path(args.record_traffic), args.copy_mib)
+        (ROOT / "profiles").mkdir(exist_ok=True)
+        (ROOT / "profiles" / "hbm_traffic.json").write_text(json.dumps(rec, indent=1) + "\n")
+        print(json.dumps(rec, indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: every box here has one MI355X and the fused "
@@ -218,10 +301,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(1, args.steps))
+        return
     import channel_convolution_epilogue_amd as cce
     cce.load()
 
-    shape, head = time_workload(torch, cce, args.workload, args.steps, args.warmup, args.seed)
+    shape, head = time_workload(torch, cce, args.workload, args.steps, args.warmup, args.seed,
+                                args.prewarm)
     print(f"# {args.workload}: {head['ms_per_call']:.4f} ms/call, {head['gflops']:.1f} GFLOP/s, "
           f"{head['roofline']['frac']:.3f} of fp32 MFMA peak", file=sys.stderr, flush=True)
     ops = {}
@@ -230,8 +317,8 @@ def main():
             if name == args.workload:
                 r = head
             else:
-                _, r = time_workload(torch, cce, name, max(3, min(args.steps, 20)), min(args.warmup, 3),
-                                     args.seed)
+                _, r = time_workload(torch, cce, name, max(3, min(args.steps, 50)), min(args.warmup, 10),
+                                     args.seed, min(args.prewarm, 0.5))
                 print(f"# {name}: {r['ms_per_call']:.4f} ms/call, {r['gflops']:.1f} GFLOP/s, "
                       f"{r['roofline']['frac']:.3f} of fp32 MFMA peak", file=sys.stderr, flush=True)
             ops[name] = {"ms_per_call": round(r["ms_per_call"], 5), "gflops": round(r["gflops"], 1),
@@ -245,6 +332,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_s": args.prewarm,
         "ms_per_step": round(head["ms_per_call"], 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -8,17 +8,20 @@
 //    not used, so the matrix cores are the only units that reach the fp32
 //    peak; the contraction is dense enough (72 x 64 per pixel) to feed them.
 //  * Output pixels are numbered flat over (n, h, w) and cut into tiles of
-//    512.  A flat numbering keeps every lane's four result pixels 16-byte
+//    256.  A flat numbering keeps every lane's four result pixels 16-byte
 //    aligned even though the 126-wide rows are not, so results leave as
 //    16-byte stores, and no tile is ragged except the last one.
-//  * A tile's input rows (all 8 channels, full width) are staged in LDS once;
-//    each 16-pixel block then reads one A value per lane per K-step straight
-//    from LDS.  The K order puts the four lanes groups on four channels and
-//    one (channel half, kh, kw) per step, so the step's LDS offset is the same
-//    for all lanes.
-//  * The whole weight (72 x 64) lives in 72 VGPRs per lane, loaded once per
-//    workgroup; workgroups are persistent and take a contiguous run of tiles,
-//    so consecutive tiles (which share input rows) stay on one XCD's L2.
+//  * A tile's input rows (all 8 channels, full width) are staged in LDS;
+//    each 16-pixel block reads one A value per lane per K-step from LDS.  The
+//    K order puts the four lane groups on four input channels and one
+//    (channel half, kh, kw) per step, so the step's LDS offset is the same for
+//    all lanes.  The 72 x 64 weight sits in LDS in B-operand order: one
+//    16-byte read per K-step serves all four 16-channel blocks.
+//  * Workgroups of 8 waves are persistent (4 waves per SIMD) and take tiles
+//    round-robin, remapped so each XCD runs consecutive tiles; the next
+//    tile's input rows are loaded into registers during the current tile's
+//    MFMAs.  The waves' 16-pixel blocks interleave, so a workgroup writes
+//    one contiguous run of every channel plane per round.
 //  * Bias is the accumulator's initial value; ReLU and HardSwish are applied
 //    in registers before the store: the conv result never reaches memory.
 #include "cce_device.hpp"
@@ -33,7 +36,7 @@ constexpr int NT = CO / 16;              // 4 channel blocks of 16
 constexpr int WAVES = 8, THREADS = 64 * WAVES;
 constexpr int MT_BATCH = 2;              // 16-pixel blocks in flight per wave
 constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // weights in LDS, B-operand order (18 KB)
-constexpr int kPrefetchPasses = 4;       // 64 of a 1024-pixel tile's <= 112 staged rows (16 per pass); the rest load at store time
+constexpr int kPrefetchPasses = 4;       // a 256-pixel tile of 128-wide rows stages <= 64 rows, 16 per pass
 
 struct Conv2dArgs {
   const float *__restrict__ x;
@@ -49,12 +52,13 @@ struct Conv2dArgs {
 };
 
 // HardSwish(ReLU(v)) = r * clamp((r + 3) / 6, 0, 1) with r = max(v, 0).  For
-// v >= 0 the gate (v + 3) / 6 is at least 0.5, and for v < 0 the product is 0
-// whatever the gate, so the gate can be taken from v itself and clamped to
-// [0.5, 1]: four operations.
+// v >= 0 the gate (v + 3) / 6 is at least 0.5, and for v < 0 the result is 0
+// whatever the gate, so the gate can be taken from v itself, clamped to
+// [0.5, 1], and the ReLU applied to the (positive-gated) product:
+// max(v * gate, 0) = max(v, 0) * gate.  Four operations.
 __device__ __forceinline__ float relu_hswish(float v) {
   const float gate = __builtin_amdgcn_fmed3f(fmaf(v, 1.0f / 6.0f, 0.5f), 0.5f, 1.0f);
-  return fmaxf(v, 0.0f) * gate;
+  return fmaxf(v * gate, 0.0f);
 }
 
 // Input rows of one tile: flat output pixels [q0, q0 + TILE) need input rows
@@ -268,10 +272,11 @@ int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, fl
 
   DeviceInfo dev;
   if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
-  // Tiles of 1024 pixels (8 waves x 8 blocks of 16); small problems use
-  // 256-pixel tiles so that every CU gets work.
-  const bool small = (a.Q + 1023) / 1024 < 2 * dev.num_cus;
-  const int tile = small ? 256 : 1024;
+  // Tiles of 256 pixels (8 waves x 2 blocks of 16).  Measured on MI355X at
+  // N = 128: 256-pixel tiles 0.222 ms, 512: 0.227 ms, 1024: 0.234 ms -- with
+  // round-robin tiles, smaller tiles keep the concurrently written stretches
+  // of each output plane closer together.
+  const int tile = 256;
   a.ntiles = (a.Q + tile - 1) / tile;
 
   // Upper bound on the input rows one tile touches: output rows spanned plus
@@ -287,16 +292,10 @@ int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, fl
 
   const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
   const bool vs = (a.P % 4 == 0) && ((uintptr_t)y % 16 == 0);
-  if (small) {
-    if (vl) return vs ? launch_instance<2, true, true>(a, R_max, stream)
-                      : launch_instance<2, true, false>(a, R_max, stream);
-    return vs ? launch_instance<2, false, true>(a, R_max, stream)
-              : launch_instance<2, false, false>(a, R_max, stream);
-  }
-  if (vl) return vs ? launch_instance<8, true, true>(a, R_max, stream)
-                    : launch_instance<8, true, false>(a, R_max, stream);
-  return vs ? launch_instance<8, false, true>(a, R_max, stream)
-            : launch_instance<8, false, false>(a, R_max, stream);
+  if (vl) return vs ? launch_instance<2, true, true>(a, R_max, stream)
+                    : launch_instance<2, true, false>(a, R_max, stream);
+  return vs ? launch_instance<2, false, true>(a, R_max, stream)
+            : launch_instance<2, false, false>(a, R_max, stream);
 }
 
 }  // namespace cce
