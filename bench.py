@@ -200,7 +200,9 @@ def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0):
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / steps  # one launch per step
+    # The calls run back to back on one stream, so the region's GPU time over K
+    # is both the step time and the average duration of the step's kernel(s).
+    kernel_ms = ev0.elapsed_time(ev1) / steps
     wc = work_counts(shape)
     out = {
         "ms_per_call": kernel_ms,
