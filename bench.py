@@ -33,7 +33,8 @@ import numpy as np
 ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
-from conv_inputs import CONV2D, CONV3D, CONVT, WORKLOADS, workload_inputs  # noqa: E402
+from conv_inputs import (CONV2D, CONV3D, CONVT, TAIL_GELU, TAIL_POOL, WORKLOADS,  # noqa: E402
+                         workload_inputs)
 
 METRIC = "fused conv+epilogue ms per call, GFLOP/s & % of fp32/HBM roofline (1 MI355X)"
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
@@ -44,13 +45,24 @@ KERNEL_SOURCES = {
     CONV2D: "conv2d_relu_hswish.hip",
     CONV3D: "conv3d_lrelu_add_clamp_gelu.hip",
     CONVT: "convT2d_pool_htanh_mean_tanh.hip",
+    TAIL_POOL: "pool_htanh_mean_tanh.hip",
+    TAIL_GELU: "lrelu_add_clamp_gelu.hip",
 }
+HBM_BOUND = (TAIL_POOL, TAIL_GELU)  # the epilogue-only operators move bytes, not FLOPs
 
 
 def work_counts(shape: dict) -> dict:
     """Algorithmic work of one call: multiply-adds of the convolution (epilogue
-    excluded) and bytes that must cross HBM (read x, w, b, s once; write y once)."""
-    op, N, Ci, Co, k = shape["op"], shape["N"], shape["C_in"], shape["C_out"], shape["k"]
+    excluded) and bytes that must cross HBM (read x, w, b, s once; write y once).
+    The epilogue-only operators have no convolution: bytes only."""
+    op = shape["op"]
+    if op == TAIL_POOL:
+        n = shape["N"] * shape["C"]
+        return {"fma": 0, "flop": 0, "bytes": 4 * (n * shape["H"] * shape["W"] + n)}
+    if op == TAIL_GELU:
+        n = shape["N"] * shape["C"] * shape["D"] * shape["H"] * shape["W"]
+        return {"fma": 0, "flop": 0, "bytes": 4 * (2 * n + shape["C"])}
+    N, Ci, Co, k = shape["N"], shape["C_in"], shape["C_out"], shape["k"]
     if op == CONV2D:
         Ho, Wo = shape["H"] - k + 1, shape["W"] - k + 1
         outs = N * Co * Ho * Wo
@@ -93,6 +105,8 @@ DOMINANT_KERNEL = {  # substring of the kernel symbol that dominates each operat
     CONV2D: "conv2d_relu_hswish_kernel",
     CONV3D: "conv3d_lrelu_add_clamp_gelu_kernel",
     CONVT: "convT2d_pool_htanh_mean_tanh_kernel",
+    TAIL_POOL: "::pool_htanh_mean_tanh_kernel",
+    TAIL_GELU: "::lrelu_add_clamp_gelu_kernel",
 }
 COPY_KERNEL = "copyBuffer"  # torch's device-to-device copy under ROCm
 
@@ -151,6 +165,12 @@ def copy_probe(mib: int, reps: int) -> None:
 
 def run_op(cce, shape, d):
     op = shape["op"]
+    if op == TAIL_POOL:
+        return lambda: cce.pool_htanh_mean_tanh(d["z"], htanh_lo=shape["lo"], htanh_hi=shape["hi"],
+                                                out=d["y"])
+    if op == TAIL_GELU:
+        return lambda: cce.lrelu_add_clamp_gelu(d["z"], d["s"], shape["slope"], shape["lo"], shape["hi"],
+                                                out=d["y"])
     if op == CONV2D:
         return lambda: cce.conv2d_relu_hswish(d["x"], d["w"], d["b"], out=d["y"])
     if op == CONV3D:
@@ -163,6 +183,12 @@ def run_op(cce, shape, d):
 
 def device_inputs(torch, cce, shape, p):
     d = {k: torch.from_numpy(v).cuda() for k, v in p.items()}
+    if shape["op"] == TAIL_POOL:
+        d["y"] = torch.empty((shape["N"], shape["C"], 1, 1), device="cuda")
+        return d
+    if shape["op"] == TAIL_GELU:
+        d["y"] = torch.empty_like(d["z"])
+        return d
     N, Co, k = shape["N"], shape["C_out"], shape["k"]
     if shape["op"] == CONV2D:
         d["y"] = torch.empty((N, Co, shape["H"] - k + 1, shape["W"] - k + 1), device="cuda")
@@ -212,10 +238,15 @@ def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0):
         "fma": wc["fma"],
         "algorithmic_bytes": wc["bytes"],
     }
-    tflops = wc["flop"] / (kernel_ms * 1e-3) / 1e12
-    out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
-                       "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
-                       "traffic": measured_traffic(shape["op"], name)}
+    if shape["op"] in HBM_BOUND:
+        out["roofline"] = {"bound": "hbm", "achieved": round(out["gbs"], 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(out["gbs"] / PEAK_HBM_GBS, 4),
+                           "traffic": measured_traffic(shape["op"], name)}
+    else:
+        tflops = wc["flop"] / (kernel_ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+                           "traffic": measured_traffic(shape["op"], name)}
     out["hbm_frac"] = round(out["gbs"] / PEAK_HBM_GBS, 4)
     del d
     torch.cuda.empty_cache()
@@ -230,6 +261,22 @@ def cpu_baseline(name, seed, budget_s=12.0):
     op = shape["op"]
     cores = O.num_threads()
     rng = np.random.default_rng(seed)
+    if op in HBM_BOUND:
+        # whole images of the epilogue-only operators, reported as GB/s of the same byte count
+        per_image = work_counts(dict(shape, N=1))["bytes"]
+        run = ((lambda z: O.pool_htanh_mean_tanh(z, shape["pool_k"], shape["pool_s"], shape["lo"], shape["hi"]))
+               if op == TAIL_POOL else
+               (lambda z: O.lrelu_add_clamp_gelu_array(z, p["s"], shape["slope"], shape["lo"], shape["hi"])))
+        t = time.perf_counter()
+        run(np.ascontiguousarray(p["z"][:1]))
+        one = time.perf_counter() - t
+        n = int(max(1, min(shape["N"], budget_s / max(one, 1e-6))))
+        zs = np.ascontiguousarray(p["z"][:n])
+        t = time.perf_counter()
+        run(zs)
+        dt = time.perf_counter() - t
+        return {"value": round(per_image * n / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
+                "kind": "oracle", "sample": f"{n} of {shape['N']} images", "seconds": round(dt, 3)}
     if op in (CONV2D, CONV3D):
         # whole images, as many as fit the time budget (at least one)
         per_image = work_counts(dict(shape, N=1))["fma"]
@@ -312,7 +359,8 @@ def main():
     shape, head = time_workload(torch, cce, args.workload, args.steps, args.warmup, args.seed,
                                 args.prewarm)
     print(f"# {args.workload}: {head['ms_per_call']:.4f} ms/call, {head['gflops']:.1f} GFLOP/s, "
-          f"{head['roofline']['frac']:.3f} of fp32 MFMA peak", file=sys.stderr, flush=True)
+          f"{head['gbs']:.1f} GB/s, {head['roofline']['frac']:.3f} of the {head['roofline']['bound']} roofline",
+          file=sys.stderr, flush=True)
     ops = {}
     if args.ops == "all":
         for name in WORKLOADS:
@@ -322,9 +370,11 @@ def main():
                 _, r = time_workload(torch, cce, name, max(3, min(args.steps, 50)), min(args.warmup, 10),
                                      args.seed, min(args.prewarm, 0.5))
                 print(f"# {name}: {r['ms_per_call']:.4f} ms/call, {r['gflops']:.1f} GFLOP/s, "
-                      f"{r['roofline']['frac']:.3f} of fp32 MFMA peak", file=sys.stderr, flush=True)
+                      f"{r['gbs']:.1f} GB/s, {r['roofline']['frac']:.3f} of the "
+                      f"{r['roofline']['bound']} roofline", file=sys.stderr, flush=True)
             ops[name] = {"ms_per_call": round(r["ms_per_call"], 5), "gflops": round(r["gflops"], 1),
-                         "gbs": round(r["gbs"], 1), "roofline_frac": r["roofline"]["frac"],
+                         "gbs": round(r["gbs"], 1), "roofline_bound": r["roofline"]["bound"],
+                         "roofline_frac": r["roofline"]["frac"],
                          "hbm_frac": r["hbm_frac"]}
 
     line = {

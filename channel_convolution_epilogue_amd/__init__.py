@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     convT2d_pool_htanh_mean_tanh,
     convT2d_pool_htanh_mean_tanh_workspace_bytes,
     library_path,
+    lrelu_add_clamp_gelu,
+    pool_htanh_mean_tanh,
     load,
     status_string,
     EXPORTED_SYMBOLS,

@@ -15,6 +15,8 @@ EXPORTED_SYMBOLS = (
     "conv3d_lrelu_add_clamp_gelu",
     "convT2d_pool_htanh_mean_tanh",
     "convT2d_pool_htanh_mean_tanh_workspace_bytes",
+    "lrelu_add_clamp_gelu",
+    "pool_htanh_mean_tanh",
 )
 
 _lib = None
@@ -57,6 +59,10 @@ def load() -> ctypes.CDLL:
         L.convT2d_pool_htanh_mean_tanh.argtypes = [fp] * 4 + [i] * 10 + [f, f, vp, sz, vp]
         L.convT2d_pool_htanh_mean_tanh_workspace_bytes.restype = sz
         L.convT2d_pool_htanh_mean_tanh_workspace_bytes.argtypes = [i] * 10
+        L.pool_htanh_mean_tanh.restype = i
+        L.pool_htanh_mean_tanh.argtypes = [fp, fp] + [i] * 6 + [f, f, vp]
+        L.lrelu_add_clamp_gelu.restype = i
+        L.lrelu_add_clamp_gelu.argtypes = [fp, fp, fp, i, i, ctypes.c_longlong, f, f, f, vp]
         _lib = L
         return L
 
@@ -177,4 +183,36 @@ def convT2d_pool_htanh_mean_tanh(x, w, b=None, stride=1, padding=1, pool_k=2, po
                                         padding, pool_k, pool_s, float(htanh_lo), float(htanh_hi),
                                         workspace.data_ptr(), ws_bytes, stream)
     _check("convT2d_pool_htanh_mean_tanh", st)
+    return out
+
+
+def pool_htanh_mean_tanh(z, pool_k=2, pool_s=2, htanh_lo=-1.0, htanh_hi=1.0, out=None):
+    """tanh(mean_{H,W}(Hardtanh(MaxPool2d(z)))) over a precomputed z [N, C, H, W] -> [N, C, 1, 1]."""
+    import torch
+    L = load()
+    N, C, H, W = z.shape
+    if out is None:
+        out = torch.empty((N, C, 1, 1), device=z.device, dtype=torch.float32)
+    st = L.pool_htanh_mean_tanh(_dev_ptr(z, "z", 4), _dev_ptr(out, "out", 4), N, C, H, W, pool_k,
+                                pool_s, float(htanh_lo), float(htanh_hi), _stream(z))
+    _check("pool_htanh_mean_tanh", st)
+    return out
+
+
+def lrelu_add_clamp_gelu(z, s, negative_slope=0.2, clamp_lo=-1.0, clamp_hi=1.0, out=None):
+    """GELU(clamp(LeakyReLU(z) + s[c], lo, hi)) elementwise over z [N, C, ...] (s has C values)."""
+    import torch
+    L = load()
+    if z.dim() < 2:
+        raise ValueError("z must be [N, C, ...]")
+    N, C = z.shape[0], z.shape[1]
+    S = z.numel() // (N * C) if z.numel() else 0
+    if s.numel() != C:
+        raise ValueError("s must hold one value per channel")
+    s = s.reshape(C)
+    if out is None:
+        out = torch.empty_like(z)
+    st = L.lrelu_add_clamp_gelu(_dev_ptr(z, "z"), _dev_ptr(s, "s", 1), _dev_ptr(out, "out"), N, C, S,
+                                float(negative_slope), float(clamp_lo), float(clamp_hi), _stream(z))
+    _check("lrelu_add_clamp_gelu", st)
     return out

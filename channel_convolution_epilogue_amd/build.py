@@ -26,6 +26,8 @@ SOURCES = [
     "conv2d_relu_hswish.hip",
     "conv3d_lrelu_add_clamp_gelu.hip",
     "convT2d_pool_htanh_mean_tanh.hip",
+    "pool_htanh_mean_tanh.hip",
+    "lrelu_add_clamp_gelu.hip",
 ]
 
 ARCH = "gfx950"

@@ -33,6 +33,12 @@ int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const fl
                                         int N, int H, int W, float lo, float hi, void *workspace,
                                         hipStream_t stream);
 
+// Epilogue-only operators over a precomputed convolution output.
+int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, float lo,
+                                float hi, hipStream_t stream);
+int launch_lrelu_add_clamp_gelu(const float *z, const float *s, float *y, int N, int C, long long S,
+                                float slope, float lo, float hi, hipStream_t stream);
+
 // Map the runtime's last error after a launch onto a cce_status.
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? CCE_OK : CCE_ERR_LAUNCH;

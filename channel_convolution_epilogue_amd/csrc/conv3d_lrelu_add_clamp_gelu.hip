@@ -49,42 +49,6 @@ struct Conv3dArgs {
   FastDiv divDo, divRowtiles, divWo;
 };
 
-// GELU(t) = 0.5 t (1 + erf(t / sqrt 2)) for |t| <= 1, from the Maclaurin series
-//   erf(z) = (2 / sqrt(pi)) sum_n (-1)^n z^(2n+1) / (n! (2n + 1))
-// (Abramowitz & Stegun 7.1.5).  With u = t^2 and z = t / sqrt 2,
-//   GELU(t) = 0.5 t + u * R(u),   R(u) = sum_n r_n u^n,
-//   r_n = (-1)^n / (sqrt(2 pi) n! (2n + 1) 2^n).
-// The series alternates with decreasing terms for |z| < 1, so stopping after
-// n = 7 errs by less than the n = 8 term: 2/sqrt(pi) z^17 / (8! 17) < 5e-9 at
-// |z| = 1/sqrt 2 -- below fp32 rounding of the result.
-constexpr double gelu_series_coef(int n) {
-  double c = 0.3989422804014327;  // 1 / sqrt(2 pi)
-  for (int k = 1; k <= n; ++k) c *= -1.0 / (2.0 * k);
-  return c / (2 * n + 1);
-}
-__device__ __forceinline__ float gelu_small(float t) {
-  const float u = t * t;
-  float r = (float)gelu_series_coef(7);
-  r = fmaf(r, u, (float)gelu_series_coef(6));
-  r = fmaf(r, u, (float)gelu_series_coef(5));
-  r = fmaf(r, u, (float)gelu_series_coef(4));
-  r = fmaf(r, u, (float)gelu_series_coef(3));
-  r = fmaf(r, u, (float)gelu_series_coef(2));
-  r = fmaf(r, u, (float)gelu_series_coef(1));
-  r = fmaf(r, u, (float)gelu_series_coef(0));
-  return fmaf(u, r, 0.5f * t);
-}
-
-// LeakyReLU -> + s -> clamp -> GELU.  SERIES: the clamp bounds lie in [-1, 1],
-// so the series above applies; otherwise the device library's erff.
-template <bool SERIES>
-__device__ __forceinline__ float epilogue(float v, float s, float slope, float lo, float hi) {
-  float t = v >= 0.0f ? v : slope * v;
-  t = clampf(t + s, lo, hi);
-  if (SERIES) return gelu_small(t);
-  return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
-}
-
 // One tile: output depth plane d of image n, output rows h0 .. h0 + rows - 1.
 // Tiles are numbered with d fastest, so a run of consecutive tiles walks down
 // the depth axis of one row block and each step needs one new input plane.
@@ -212,10 +176,10 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
         if (v0 >= V) continue;
         float *dst = ybase + (size_t)o * vol + v0;
         v4f r = acc[j];
-        r.x = epilogue<SERIES>(r.x, sadd, a.slope, a.lo, a.hi);
-        r.y = epilogue<SERIES>(r.y, sadd, a.slope, a.lo, a.hi);
-        r.z = epilogue<SERIES>(r.z, sadd, a.slope, a.lo, a.hi);
-        r.w = epilogue<SERIES>(r.w, sadd, a.slope, a.lo, a.hi);
+        r.x = lrelu_add_clamp_gelu_value<SERIES>(r.x, sadd, a.slope, a.lo, a.hi);
+        r.y = lrelu_add_clamp_gelu_value<SERIES>(r.y, sadd, a.slope, a.lo, a.hi);
+        r.z = lrelu_add_clamp_gelu_value<SERIES>(r.z, sadd, a.slope, a.lo, a.hi);
+        r.w = lrelu_add_clamp_gelu_value<SERIES>(r.w, sadd, a.slope, a.lo, a.hi);
         if (VSTORE && v0 + 3 < V) {
           store4(dst, r);
         } else {

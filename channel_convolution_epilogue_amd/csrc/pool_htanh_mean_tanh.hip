@@ -1,0 +1,112 @@
+// Epilogue-only tail of the transposed-conv model over a precomputed conv
+// output z[N][C][H][W]: y[n, c] = tanh(mean(Hardtanh(MaxPool2d(z[n, c], 2, 2)))).
+// This is the path POPCORNBENCH Kimi-K2.6 l2_p10 implemented (a library
+// transposed convolution followed by one fused tail kernel); here it is the
+// HBM-read-bound companion of the fully fused operator.
+//
+// Design: one workgroup per (n, c) plane streams the plane once.  With W a
+// multiple of 4, each thread takes a column quad of a row pair: two 16-byte
+// loads give two 2x2 windows.  Consecutive threads read consecutive quads, so
+// a wave reads 1 KB of a row per load.  Loads are issued four pairs ahead.
+// Window sums are reduced in a fixed order (lane -> wave -> workgroup), so the
+// result is deterministic.
+#include "cce_device.hpp"
+#include "cce_internal.hpp"
+
+namespace cce {
+namespace {
+
+constexpr int THREADS = 256, WAVES = THREADS / 64;
+
+struct TailArgs {
+  const float *__restrict__ z;
+  float *__restrict__ y;
+  int H, W, PH, PW;
+  float lo, hi, inv_count;
+};
+
+__device__ __forceinline__ float window(float a, float b, float c, float d, float lo, float hi) {
+  return clampf(fmaxf(fmaxf(a, b), fmaxf(c, d)), lo, hi);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(THREADS) void pool_htanh_mean_tanh_kernel(TailArgs a) {
+  __shared__ float red[WAVES];
+  const float *plane = a.z + (size_t)blockIdx.x * a.H * a.W;
+  float sum = 0.0f;
+  if (VEC) {
+    // unit u = (ph, q): rows 2ph and 2ph + 1, columns 4q .. 4q + 3 (windows 2q, 2q + 1)
+    const int QW = a.PW >> 1;  // W % 4 == 0, so PW is even and QW = W / 4
+    const int units = a.PH * QW;
+    constexpr int UNROLL = 4;
+    int u = threadIdx.x;
+    for (; u + (UNROLL - 1) * THREADS < units; u += UNROLL * THREADS) {
+      v4f r0[UNROLL], r1[UNROLL];
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        const int uu = u + k * THREADS, ph = uu / QW, q = uu - ph * QW;
+        const float *p = plane + (size_t)(2 * ph) * a.W + 4 * q;
+        r0[k] = *reinterpret_cast<const v4f *>(p);
+        r1[k] = *reinterpret_cast<const v4f *>(p + a.W);
+      }
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        sum += window(r0[k].x, r0[k].y, r1[k].x, r1[k].y, a.lo, a.hi);
+        sum += window(r0[k].z, r0[k].w, r1[k].z, r1[k].w, a.lo, a.hi);
+      }
+    }
+    for (; u < units; u += THREADS) {
+      const int ph = u / QW, q = u - ph * QW;
+      const float *p = plane + (size_t)(2 * ph) * a.W + 4 * q;
+      const v4f r0 = *reinterpret_cast<const v4f *>(p);
+      const v4f r1 = *reinterpret_cast<const v4f *>(p + a.W);
+      sum += window(r0.x, r0.y, r1.x, r1.y, a.lo, a.hi);
+      sum += window(r0.z, r0.w, r1.z, r1.w, a.lo, a.hi);
+    }
+  } else {
+    const int units = a.PH * a.PW;  // one window each; floor pooling drops an odd last row/column
+    for (int u = threadIdx.x; u < units; u += THREADS) {
+      const int ph = u / a.PW, pw = u - ph * a.PW;
+      const float *p = plane + (size_t)(2 * ph) * a.W + 2 * pw;
+      sum += window(p[0], p[1], p[a.W], p[a.W + 1], a.lo, a.hi);
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) tot += red[w];
+    a.y[blockIdx.x] = tanhf(tot * a.inv_count);
+  }
+}
+
+}  // namespace
+
+int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, float lo,
+                                float hi, hipStream_t stream) {
+  TailArgs a;
+  a.z = z;
+  a.y = y;
+  a.H = H;
+  a.W = W;
+  a.PH = H / 2;
+  a.PW = W / 2;
+  a.lo = lo;
+  a.hi = hi;
+  a.inv_count = (float)(1.0 / ((double)a.PH * (double)a.PW));
+  const long long planes = (long long)N * C;
+  if (planes >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
+  const bool vec = (W % 4 == 0) && ((uintptr_t)z % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL(pool_htanh_mean_tanh_kernel<true>, dim3((unsigned)planes), dim3(THREADS), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(pool_htanh_mean_tanh_kernel<false>, dim3((unsigned)planes), dim3(THREADS), 0,
+                       stream, a);
+  return launch_status();
+}
+
+}  // namespace cce

@@ -136,6 +136,39 @@ size_t convT2d_pool_htanh_mean_tanh_workspace_bytes(int N, int C_in, int H, int 
                                                     int k, int stride, int pad, int pool_k,
                                                     int pool_s);
 
+/*
+ * Epilogue-only operators over a precomputed convolution output (the
+ * unfused paths the pages fall back to; the fused operators above do not
+ * need them).
+ */
+
+/*
+ * y[n,c] = tanh(mean_{ph,pw} Hardtanh(MaxPool2d(z[n,c], pool_k, pool_s)))  -- page l2_p10's
+ * fused tail over a library transposed-conv output
+ *
+ *   z  [N][C][H][W]   e.g. the transposed-conv output
+ *   y  [N][C]         (the [N,C,1,1] result)
+ *
+ * Pooled size floor((H - pool_k) / pool_s) + 1 per axis; the mean divides by
+ * the pooled element count.  Deterministic (fixed summation order).
+ * Supported: pool_k = pool_s = 2, H, W >= 2, htanh_lo <= htanh_hi (finite),
+ * N*C < 2^31.
+ */
+int pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, int pool_k,
+                         int pool_s, float htanh_lo, float htanh_hi, void *stream);
+
+/*
+ * y = GELU(clamp(LeakyReLU(z, slope) + s[c], lo, hi)) elementwise  -- page l2_p90's
+ * fallback after a library Conv3d
+ *
+ *   z, y  [N][C][S]   S = spatial elements per channel (e.g. D*H*W); y may equal z
+ *   s     [C]         per-channel offset (the [C,1,1,1] sum_tensor)
+ *
+ * Supported: N, C, S >= 1, lo <= hi, all three scalars finite, N*C < 2^31.
+ */
+int lrelu_add_clamp_gelu(const float *z, const float *s, float *y, int N, int C, long long S,
+                         float negative_slope, float clamp_lo, float clamp_hi, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

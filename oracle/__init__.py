@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_convT2d_gather.argtypes = [_f, _f, _f, _d] + [_c_int] * 8
         L.oracle_pool_htanh_mean_tanh_plane.restype = _c_dbl
         L.oracle_pool_htanh_mean_tanh_plane.argtypes = [_d] + [_c_int] * 4 + [_c_dbl] * 2
+        L.oracle_pool_htanh_mean_tanh.argtypes = [_d, _d] + [_c_int] * 6 + [_c_dbl] * 2
+        L.oracle_pool_htanh_mean_tanh_f32.argtypes = [_f, _d] + [_c_int] * 6 + [_c_dbl] * 2
+        L.oracle_lrelu_add_clamp_gelu_f32.argtypes = [_f, _f, _d, _c_int, _c_int, ctypes.c_int64] + [_c_dbl] * 3
         L.oracle_convT2d_pool_htanh_mean_tanh_at.argtypes = (
             [_f, _f, _f] + [_c_int] * 10 + [_c_dbl] * 2 + [_i64, ctypes.c_int64, _d, ctypes.c_int64, _d])
         _lib = L
@@ -251,3 +254,31 @@ def convT2d_pool_htanh_mean_tanh(x, w, b=None, stride=1, pad=1, pk=2, ps=2, lo=-
     C_out = w.shape[1]
     y = convT2d_pool_htanh_mean_tanh_at(x, w, b, np.arange(N * C_out), stride, pad, pk, ps, lo, hi)
     return y.reshape(N, C_out)
+
+
+# -- epilogue-only operators over a precomputed convolution output -------------
+
+def pool_htanh_mean_tanh(z, pk=2, ps=2, lo=-1.0, hi=1.0):
+    """Tail of the transposed-conv model on z[N, C, H, W] (float32 or float64) -> [N, C]."""
+    N, C, H, W = z.shape
+    y = np.empty((N, C), np.float64)
+    if z.dtype == np.float32:
+        _check(lib().oracle_pool_htanh_mean_tanh_f32(_fp(np.ascontiguousarray(z)), _dp(y), N, C, H, W,
+                                                     pk, ps, lo, hi), "pool_htanh_mean_tanh")
+    else:
+        zd = np.ascontiguousarray(z, dtype=np.float64)
+        _check(lib().oracle_pool_htanh_mean_tanh(_dp(zd), _dp(y), N, C, H, W, pk, ps, lo, hi),
+               "pool_htanh_mean_tanh")
+    return y
+
+
+def lrelu_add_clamp_gelu_array(z, s, slope=0.2, lo=-1.0, hi=1.0):
+    """Elementwise epilogue of the Conv3d model on z[N, C, ...] (float32) with s[C]."""
+    N, C = z.shape[:2]
+    S = int(np.prod(z.shape[2:])) if z.ndim > 2 else 1
+    zz = np.ascontiguousarray(z, dtype=np.float32)
+    ss = np.ascontiguousarray(np.asarray(s, np.float32).reshape(-1))
+    y = np.empty(z.shape, np.float64)
+    _check(lib().oracle_lrelu_add_clamp_gelu_f32(_fp(zz), _fp(ss), _dp(y), N, C, S, slope, lo, hi),
+           "lrelu_add_clamp_gelu")
+    return y

@@ -417,3 +417,65 @@ int oracle_convT2d_pool_htanh_mean_tanh_at(const float *x, const float *w, const
   }
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Epilogue-only operators over a precomputed convolution output            */
+/* ------------------------------------------------------------------------ */
+
+/* l2_p10's fused tail, the path that page implemented after a library
+ * transposed conv: y[n,c] = tanh(mean(Hardtanh(MaxPool2d(z[n,c])))) for every
+ * (n, c) plane of z[N][C][H][W].  Each plane goes through the same plane
+ * function as the fused model above. */
+int oracle_pool_htanh_mean_tanh(const double *z, double *y, int N, int C, int H, int W, int pk,
+                                int ps, double lo, double hi) {
+  if (!z || !y || N < 1 || C < 1 || pk < 1 || ps < 1) return ORACLE_EBADARG;
+  if (oracle_pool_out_size(H, pk, ps) < 1 || oracle_pool_out_size(W, pk, ps) < 1) return ORACLE_EBADARG;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int c = 0; c < C; ++c)
+      y[(size_t)n * C + c] =
+          oracle_pool_htanh_mean_tanh_plane(z + ((size_t)n * C + c) * H * W, H, W, pk, ps, lo, hi);
+  return ORACLE_OK;
+}
+
+/* Same tail reading fp32 input (what the GPU operator consumes). */
+int oracle_pool_htanh_mean_tanh_f32(const float *z, double *y, int N, int C, int H, int W, int pk,
+                                    int ps, double lo, double hi) {
+  if (!z || !y || N < 1 || C < 1 || H < 1 || W < 1 || pk < 1 || ps < 1) return ORACLE_EBADARG;
+  if (oracle_pool_out_size(H, pk, ps) < 1 || oracle_pool_out_size(W, pk, ps) < 1) return ORACLE_EBADARG;
+  int PH = oracle_pool_out_size(H, pk, ps), PW = oracle_pool_out_size(W, pk, ps);
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int c = 0; c < C; ++c) {
+      const float *zp = z + ((size_t)n * C + c) * H * W;
+      double sum = 0.0;
+      for (int ph = 0; ph < PH; ++ph)
+        for (int pw = 0; pw < PW; ++pw) {
+          double m = zp[(size_t)(ph * ps) * W + (pw * ps)];
+          for (int dh = 0; dh < pk; ++dh)
+            for (int dw = 0; dw < pk; ++dw) {
+              double v = zp[(size_t)(ph * ps + dh) * W + (pw * ps + dw)];
+              if (v > m) m = v;
+            }
+          sum += oracle_clamp(m, lo, hi);
+        }
+      y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)PW));
+    }
+  return ORACLE_OK;
+}
+
+/* l2_p90's elementwise fallback after a library Conv3d: for z[N][C][S] (S =
+ * spatial elements per channel), y = GELU(clamp(LeakyReLU(z) + s[c], lo, hi)),
+ * each element through the same scalar epilogue as the fused model. */
+int oracle_lrelu_add_clamp_gelu_f32(const float *z, const float *s, double *y, int N, int C,
+                                    int64_t S, double slope, double lo, double hi) {
+  if (!z || !s || !y || N < 1 || C < 1 || S < 1) return ORACLE_EBADARG;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int c = 0; c < C; ++c) {
+      const size_t base = ((size_t)n * C + c) * (size_t)S;
+      for (int64_t e = 0; e < S; ++e)
+        y[base + e] = oracle_lrelu_add_clamp_gelu((double)z[base + e], (double)s[c], slope, lo, hi);
+    }
+  return ORACLE_OK;
+}

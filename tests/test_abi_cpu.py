@@ -128,3 +128,23 @@ def test_binding_rejects_cpu_tensors():
     w = torch.zeros(64, 8, 3, 3)
     with pytest.raises(TypeError):
         cce.conv2d_relu_hswish(x, w, None, out=torch.zeros(1, 64, 6, 6))
+
+
+def test_tail_validation(lib):
+    def pt(z=FAKE, y=FAKE, N=2, C=3, H=8, W=8, pk=2, ps=2, lo=-1.0, hi=1.0):
+        return lib.pool_htanh_mean_tanh(z, y, N, C, H, W, pk, ps, lo, hi, None)
+    assert pt(z=None) == ENULL
+    assert pt(H=1) == ESHAPE
+    assert pt(N=0) == ESHAPE
+    assert pt(pk=3, ps=3) == EUNSUP
+    assert pt(lo=1.0, hi=0.0) == EUNSUP
+    assert pt(y=FAKE + 1) == EALIGN
+    assert pt(N=1 << 20, C=1 << 12) == ETOOBIG
+
+    def lt(z=FAKE, s=FAKE, y=FAKE, N=2, C=3, S=10, slope=0.2, lo=-1.0, hi=1.0):
+        return lib.lrelu_add_clamp_gelu(z, s, y, N, C, S, slope, lo, hi, None)
+    assert lt(s=None) == ENULL
+    assert lt(S=0) == ESHAPE
+    assert lt(hi=float("nan")) == EUNSUP
+    assert lt(z=FAKE + 2) == EALIGN
+    assert lt(S=1 << 41) == ETOOBIG

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from conv_inputs import CONV2D, CONV3D, CONVT, make_inputs, workload_inputs
+from conv_inputs import CONV2D, CONV3D, CONVT, TAIL_GELU, TAIL_POOL, make_inputs, workload_inputs
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -222,3 +222,55 @@ def test_convT_workload_sampled(cce, name, count):
     idx = np.unique(np.concatenate([rng.integers(0, yh.size, count), [0, yh.size - 1]]))
     ref = O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], idx)
     assert_close(yh.reshape(-1)[idx], ref, f"{name} sampled")
+
+
+# ---------------------------------------------------------------------------
+# Epilogue-only operators over a precomputed convolution output
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,C,H,W", [(2, 3, 256, 256), (3, 2, 37, 23), (1, 1, 2, 2), (2, 5, 20, 30),
+                                     (4, 64, 64, 64)])
+def test_pool_tail_small(cce, N, C, H, W):
+    p = make_inputs(TAIL_POOL, seed=400 + N * C, N=N, C=C, H=H, W=W)
+    z = p["z"] * np.float32(0.7)
+    y = cce.pool_htanh_mean_tanh(dev(z))
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy()[:, :, 0, 0], O.pool_htanh_mean_tanh(z), f"pool tail N={N} C={C} {H}x{W}")
+
+
+def test_pool_tail_workload_full(cce):
+    shape, p = workload_inputs("pool_htanh_mean_tanh_n128", seed=0)
+    y = cce.pool_htanh_mean_tanh(dev(p["z"]))
+    y2 = cce.pool_htanh_mean_tanh(dev(p["z"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y2.cpu().numpy())
+    assert_close(y.cpu().numpy()[:, :, 0, 0], O.pool_htanh_mean_tanh(p["z"]), "pool tail n128 full")
+
+
+@pytest.mark.parametrize("N,C,D,H,W", [(2, 64, 3, 10, 12), (1, 3, 1, 1, 7), (3, 5, 2, 9, 11),
+                                       (1, 64, 14, 62, 62)])
+def test_elementwise_tail_small(cce, N, C, D, H, W):
+    p = make_inputs(TAIL_GELU, seed=500 + N * C, N=N, C=C, D=D, H=H, W=W)
+    s = p["s"] * 20
+    for slope, lo, hi in [(0.2, -1.0, 1.0), (0.1, -2.0, 3.0)]:
+        y = cce.lrelu_add_clamp_gelu(dev(p["z"]), dev(s), slope, lo, hi)
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy(), O.lrelu_add_clamp_gelu_array(p["z"], s, slope, lo, hi),
+                     f"elementwise tail {N}x{C}x{D}x{H}x{W} clamp [{lo},{hi}]")
+
+
+def test_elementwise_tail_workload_sampled(cce):
+    shape, p = workload_inputs("lrelu_add_clamp_gelu_n128", seed=0)
+    y = cce.lrelu_add_clamp_gelu(dev(p["z"]), dev(p["s"]), shape["slope"], shape["lo"], shape["hi"])
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert np.all(np.isfinite(yh)) and yh.min() >= GELU_LO - 1e-6 and yh.max() <= GELU_HI + 1e-6
+    # whole planes at the two ends plus random elements
+    idx = sample_indices(yh.size, 200000, 5)
+    zf = p["z"].reshape(-1)
+    C, S = shape["C"], yh.size // (shape["N"] * shape["C"])
+    ch = (idx // S) % C
+    ref = np.array([O.lrelu_add_clamp_gelu(zf[i], p["s"][c]) for i, c in zip(idx[:20000], ch[:20000])])
+    assert_close(yh.reshape(-1)[idx[:20000]], ref, "elementwise tail n128 sampled")
+    head = O.lrelu_add_clamp_gelu_array(p["z"][:1], p["s"])
+    assert_close(yh[:1], head, "elementwise tail n128 first image")

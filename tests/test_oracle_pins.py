@@ -424,3 +424,41 @@ def test_input_recipe_distributions():
     assert all(np.array_equal(p[k], q[k]) for k in p)
     t = make_inputs(CONVT, seed=1, N=1, C_in=64, H=4, W=4, C_out=64, k=3)
     assert t["w"].shape == (64, 64, 3, 3) and t["w"].max() <= 1 / 24
+
+
+# ---------------------------------------------------------------------------
+# Epilogue-only operators over a precomputed convolution output
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(2, 3, 8, 8), (1, 2, 7, 9), (2, 1, 2, 2), (1, 4, 5, 12)])
+def test_pool_tail_matches_torch_and_plane_function(shape):
+    rng = np.random.default_rng(20 + sum(shape))
+    z = (rng.standard_normal(shape) * 1.5).astype(np.float32)
+    ref = torch.tanh(F.hardtanh(F.max_pool2d(_t64(z), 2, 2), -1, 1).mean(dim=(2, 3))).numpy()
+    np.testing.assert_allclose(O.pool_htanh_mean_tanh(z), ref, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(O.pool_htanh_mean_tanh(z.astype(np.float64)), ref, rtol=0, atol=1e-14)
+    n, c = shape[0] - 1, shape[1] - 1
+    assert O.pool_htanh_mean_tanh(z)[n, c] == pytest.approx(
+        O.pool_htanh_mean_tanh_plane(z[n, c].astype(np.float64)), abs=1e-15)
+    # other Hardtanh bounds
+    ref2 = torch.tanh(F.hardtanh(F.max_pool2d(_t64(z), 2, 2), -0.3, 0.7).mean(dim=(2, 3))).numpy()
+    np.testing.assert_allclose(O.pool_htanh_mean_tanh(z, lo=-0.3, hi=0.7), ref2, rtol=0, atol=1e-14)
+
+
+def test_pool_tail_of_convT_equals_fused_model():
+    # The tail over the oracle's own transposed-conv output reproduces the fused model.
+    p = make_inputs(CONVT, seed=21, N=2, C_in=64, H=6, W=10, C_out=64, k=3)
+    z = O.convT2d_gather(p["x"], p["w"], p["b"])
+    np.testing.assert_allclose(O.pool_htanh_mean_tanh(z),
+                               O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], p["b"]), rtol=0, atol=1e-15)
+
+
+def test_elementwise_tail_matches_torch_and_scalar():
+    rng = np.random.default_rng(22)
+    z = (rng.standard_normal((2, 5, 3, 4, 7)) * 2).astype(np.float32)
+    s = (rng.standard_normal(5) * 0.5).astype(np.float32)
+    for slope, lo, hi in [(0.2, -1.0, 1.0), (0.05, -0.5, 2.0)]:
+        y = O.lrelu_add_clamp_gelu_array(z, s, slope, lo, hi)
+        ref = F.gelu(torch.clamp(F.leaky_relu(_t64(z), slope) + _t64(s).view(1, -1, 1, 1, 1), lo, hi)).numpy()
+        np.testing.assert_allclose(y, ref, rtol=0, atol=1e-15)
+    assert y[1, 3, 2, 1, 6] == O.lrelu_add_clamp_gelu(z[1, 3, 2, 1, 6], s[3], 0.05, -0.5, 2.0)
