@@ -1,0 +1,69 @@
+"""Host-side logic of bench.py (no GPU): algorithmic work counts, the HBM
+counter conversion, and the refusal to run on more than one GPU."""
+import csv
+import json
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+import bench
+from conv_inputs import WORKLOADS
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+def test_work_counts_match_page_counts():
+    golden = json.load(open(ROOT / "tests" / "golden" / "page_values.json"))
+    c2 = bench.work_counts(dict(WORKLOADS["conv2d_relu_hswish_n128"]))
+    assert c2["fma"] == golden["conv2d_shapes"]["out_elements"] * 72
+    assert c2["bytes"] == 4 * (128 * 8 * 128 * 128 + 64 * 72 + 64 + golden["conv2d_shapes"]["out_elements"])
+    c3 = bench.work_counts(dict(WORKLOADS["conv3d_lrelu_add_clamp_gelu_n128"]))
+    assert c3["fma"] == golden["conv3d_shapes"]["fmas"]
+    ct = bench.work_counts(dict(WORKLOADS["convT2d_pool_htanh_mean_tanh_n128"]))
+    assert ct["fma"] == golden["convT_shapes"]["macs"]
+    assert ct["flop"] == 2 * ct["fma"]
+    tp = bench.work_counts(dict(WORKLOADS["pool_htanh_mean_tanh_n128"]))
+    assert tp["fma"] == 0 and tp["bytes"] == 4 * (128 * 64 * 256 * 256 + 128 * 64)
+    tg = bench.work_counts(dict(WORKLOADS["lrelu_add_clamp_gelu_n128"]))
+    assert tg["bytes"] == 4 * (2 * golden["conv3d_shapes"]["out_elements"] + 64)
+
+
+def _write_counter_csv(path: Path, rows):
+    path.mkdir(parents=True)
+    with open(path / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_record_traffic_scales_by_copy_calibration(tmp_path):
+    mib = 64
+    # The copy reads as half its size on FETCH_SIZE and exactly on WRITE_SIZE.
+    _write_counter_csv(tmp_path / "fetch_copy", [
+        {"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "FETCH_SIZE", "Counter_Value": mib * 512}])
+    _write_counter_csv(tmp_path / "write_copy", [
+        {"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "WRITE_SIZE", "Counter_Value": mib * 1024}])
+    k = "void cce::(anonymous namespace)::conv2d_relu_hswish_kernel<2, true, true, 4>(Args)"
+    _write_counter_csv(tmp_path / "fetch_conv2d_relu_hswish_n8", [
+        {"Kernel_Name": k, "Counter_Name": "FETCH_SIZE", "Counter_Value": 100.0},
+        {"Kernel_Name": k, "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0},
+        {"Kernel_Name": "other", "Counter_Name": "FETCH_SIZE", "Counter_Value": 1e9}])
+    _write_counter_csv(tmp_path / "write_conv2d_relu_hswish_n8", [
+        {"Kernel_Name": k, "Counter_Name": "WRITE_SIZE", "Counter_Value": 50.0}])
+    rec = bench.record_traffic(tmp_path, mib)
+    assert rec["copy_scale"] == {"fetch": 2.0, "write": 1.0}
+    r = rec["conv2d_relu_hswish_n8"]
+    assert r["fetch_bytes"] == 200 * 1024 * 2 and r["write_bytes"] == 50 * 1024
+    assert r["bytes_per_launch"] == r["fetch_bytes"] + r["write_bytes"]
+    assert r["source_sha256_16"] == bench.source_digest("conv2d_relu_hswish")
+    assert "conv3d_lrelu_add_clamp_gelu_n128" not in rec
+
+
+def test_bench_refuses_more_than_one_gpu():
+    res = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "8"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
