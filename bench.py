@@ -82,8 +82,12 @@ def work_counts(shape: dict) -> dict:
 
 
 def source_digest(op: str) -> str:
-    src = ROOT / "channel_convolution_epilogue_amd" / "csrc" / KERNEL_SOURCES[op]
-    return hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    """Digest of the operator's kernel source and the device header it includes."""
+    csrc = ROOT / "channel_convolution_epilogue_amd" / "csrc"
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[op], "cce_device.hpp"):
+        h.update((csrc / name).read_bytes())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(op: str, workload: str):
@@ -118,12 +122,14 @@ def _counter_per_dispatch(csv_path: Path, kernel_substr: str, counter: str):
     return (sum(vals) / len(vals)) if vals else None
 
 
-def record_traffic(pmc_dir: Path, copy_mib: int) -> dict:
+def record_traffic(pmc_dir: Path, copy_mib: int, previous: dict | None = None) -> dict:
     """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) into HBM
     bytes per launch of each workload's dominant kernel.  Each counter is
     scaled by the factor that makes it read exactly `copy_mib` MiB for a plain
     device copy of that size.  Expects <dir>/{fetch,write}_<workload>/ and
-    <dir>/{fetch,write}_copy/ from `rocprofv3 --pmc ... --output-format csv -o run`."""
+    <dir>/{fetch,write}_copy/ from `rocprofv3 --pmc ... --output-format csv -o run`.
+    Records in `previous` for workloads not measured in this directory are
+    kept while their kernel source digest still matches."""
     known = copy_mib * 1024 * 1024
     scale = {}
     for kind, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
@@ -134,6 +140,11 @@ def record_traffic(pmc_dir: Path, copy_mib: int) -> dict:
                       "dispatch), each scaled so that a plain %d MiB device copy reads/writes "
                       "exactly %d MiB; valid while the kernel source digest matches." % (copy_mib, copy_mib)),
            "copy_scale": {k: round(v, 5) for k, v in scale.items()}}
+    for name, rec in (previous or {}).items():
+        cfg = WORKLOADS.get(name)
+        if cfg and isinstance(rec, dict) and rec.get("source_sha256_16") == source_digest(cfg["op"]):
+            rec.setdefault("copy_scale", previous.get("copy_scale"))
+            out[name] = rec
     for name, cfg in WORKLOADS.items():
         op = cfg["op"]
         f = pmc_dir / f"fetch_{name}" / "run_counter_collection.csv"
@@ -146,6 +157,7 @@ def record_traffic(pmc_dir: Path, copy_mib: int) -> dict:
         out[name] = {"kernel": DOMINANT_KERNEL[op], "source_sha256_16": source_digest(op),
                      "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
                      "bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb), "write_bytes": int(wb),
+                     "copy_scale": out["copy_scale"],
                      "algorithmic_bytes": work_counts(dict(cfg))["bytes"]}
     return out
 
@@ -334,9 +346,11 @@ def main():
     args = ap.parse_args()
 
     if args.record_traffic:
-        rec = record_traffic(Path(args.record_traffic), args.copy_mib)
-        (ROOT / "profiles").mkdir(exist_ok=True)
-        (ROOT / "profiles" / "hbm_traffic.json").write_text(json.dumps(rec, indent=1) + "\n")
+        dest = ROOT / "profiles" / "hbm_traffic.json"
+        prev = json.loads(dest.read_text()) if dest.exists() else None
+        rec = record_traffic(Path(args.record_traffic), args.copy_mib, prev)
+        dest.parent.mkdir(exist_ok=True)
+        dest.write_text(json.dumps(rec, indent=1) + "\n")
         print(json.dumps(rec, indent=1))
         return
 

@@ -75,11 +75,10 @@ int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y,
   if (!x || !w || !y) return CCE_ERR_NULL;
   if (N < 1 || C_in < 1 || C_out < 1 || k < 1 || H < k || W < k) return CCE_ERR_SHAPE;
   if (C_in != 8 || C_out != 64 || k != 3) return CCE_ERR_UNSUPPORTED;
-  if (W > 1024) return CCE_ERR_UNSUPPORTED;
   if (!aligned4(x) || !aligned4(w) || !aligned4(y) || (b && !aligned4(b))) return CCE_ERR_ALIGN;
   const long long P = (long long)(H - 2) * (W - 2);
   if ((long long)N * P >= (1LL << 31) || (long long)N * H >= (1LL << 31) ||
-      (long long)N * C_in * H * W >= (1LL << 40))
+      (long long)C_in * H * W >= (1LL << 31) || (long long)N * C_in * H * W >= (1LL << 40))
     return CCE_ERR_TOO_LARGE;
   return cce::launch_conv2d_relu_hswish(x, w, b, y, N, H, W, (hipStream_t)stream);
 }

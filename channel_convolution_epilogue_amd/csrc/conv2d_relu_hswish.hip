@@ -7,21 +7,29 @@
 //    output channels, K = 8 channels x 9 taps = 72.  Packed fp32 VALU math is
 //    not used, so the matrix cores are the only units that reach the fp32
 //    peak; the contraction is dense enough (72 x 64 per pixel) to feed them.
-//  * Output pixels are numbered flat over (n, h, w) and cut into tiles of
-//    256.  A flat numbering keeps every lane's four result pixels 16-byte
-//    aligned even though the 126-wide rows are not, so results leave as
-//    16-byte stores, and no tile is ragged except the last one.
-//  * A tile's input rows (all 8 channels, full width) are staged in LDS;
-//    each 16-pixel block reads one A value per lane per K-step from LDS.  The
-//    K order puts the four lane groups on four input channels and one
+//  * The unit of work is one wave's strip: 16 output columns by 2 output rows
+//    of one image, all 64 channels (two 16-pixel MFMA blocks).  Each wave
+//    stages its strip's input window (8 channels x 4 rows x 24 columns) in a
+//    slice of LDS of its own, so no wave ever waits for another's data.  The
+//    next strip's window is loaded into registers while the current strip's
+//    MFMAs run, and written to the wave's slice after them.
+//  * Strips are dealt in rounds, strip index fastest: in one round the 16
+//    waves of a workgroup take 16 consecutive strips, i.e. whole rows of the
+//    output (8 strips cover 126 columns), and write 4 full rows of every
+//    channel plane.  One barrier per round keeps the waves in step, so that
+//    the 64-byte pieces that neighbouring waves write into one 128-byte line
+//    reach the L2 together.  Measured on MI355X: without it, partly written
+//    lines are evicted and rewritten, which costs 1.6x more HBM traffic and
+//    makes the kernel 1.6x slower.  Consecutive workgroups take consecutive
+//    rounds, and the blockIdx remap gives each XCD a contiguous block.
+//  * Results leave as 16-byte stores.  A row's strips are shifted left by
+//    (row offset mod 4) columns so that every lane's four pixels start on a
+//    16-byte boundary even when the row length is not a multiple of four;
+//    pixels that fall outside the row are masked.
+//  * The K order puts the four lane groups on four input channels and one
 //    (channel half, kh, kw) per step, so the step's LDS offset is the same for
 //    all lanes.  The 72 x 64 weight sits in LDS in B-operand order: one
 //    16-byte read per K-step serves all four 16-channel blocks.
-//  * Workgroups of 8 waves are persistent (4 waves per SIMD) and take tiles
-//    round-robin, remapped so each XCD runs consecutive tiles; the next
-//    tile's input rows are loaded into registers during the current tile's
-//    MFMAs.  The waves' 16-pixel blocks interleave, so a workgroup writes
-//    one contiguous run of every channel plane per round.
 //  * Bias is the accumulator's initial value; ReLU and HardSwish are applied
 //    in registers before the store: the conv result never reaches memory.
 #include "cce_device.hpp"
@@ -31,24 +39,44 @@ namespace cce {
 namespace {
 
 constexpr int CI = 8, CO = 64, KS = 3, TAPS = KS * KS;
-constexpr int KSTEPS = (CI / 4) * TAPS;  // 18 steps of 4 taps
-constexpr int NT = CO / 16;              // 4 channel blocks of 16
-constexpr int WAVES = 8, THREADS = 64 * WAVES;
-constexpr int MT_BATCH = 2;              // 16-pixel blocks in flight per wave
+constexpr int KSTEPS = (CI / 4) * TAPS;      // 18 steps of 4 taps
+constexpr int NT = CO / 16;                  // 4 channel blocks of 16
+constexpr int WAVES = 16, THREADS = 64 * WAVES;  // one workgroup per CU, 4 waves per SIMD
 constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // weights in LDS, B-operand order (18 KB)
-constexpr int kPrefetchPasses = 4;       // a 256-pixel tile of 128-wide rows stages <= 64 rows, 16 per pass
+
+// Geometry of one wave's strip: RB output rows by CB blocks of 16 columns.
+// The staged window spans columns [c0 - 4, c0 + 16 CB + 4) (quad-aligned, and
+// wide enough for the 0..3 column shift and the 2-column halo) and RB + 2 rows.
+// Its channel planes are CS floats apart, CS = 16 or 48 mod 64, so the four
+// lane groups of an A read (four channels) start on four different quarters
+// of the 64 LDS banks.
+constexpr int chan_stride(int need) {
+  int c = need;
+  while (c % 64 != 16 && c % 64 != 48) ++c;
+  return c;
+}
+template <int RB_, int CB_>
+struct StripGeo {
+  static constexpr int RB = RB_, CB = CB_, MT = RB * CB;
+  static constexpr int SW = 16 * CB;         // output columns per strip
+  static constexpr int XW = SW + 8;          // staged columns per row
+  static constexpr int XQ = XW / 4;          // 16-byte quads per staged row
+  static constexpr int ROWS = RB + KS - 1;   // staged rows
+  static constexpr int CS = chan_stride(ROWS * XW);
+  static constexpr int WIN = CI * CS;        // floats per wave window
+};
 
 struct Conv2dArgs {
   const float *__restrict__ x;
   const float *__restrict__ w;
   const float *__restrict__ b;
   float *__restrict__ y;
-  int H, W, Wo;
-  int P;         // output pixels per image plane, (H-2)*(W-2)
-  int Q;         // output pixels over the batch, N*P
-  int ntiles;    // ceil(Q / tile)
-  int chstride;  // floats between channel planes in LDS
-  FastDiv divP, divWo, divH;
+  int H, W, Ho, Wo;
+  int P;       // output pixels per plane, Ho * Wo
+  int S;       // strips per row group, ceil((Wo + largest shift) / strip width)
+  int G;       // row groups per image, ceil(Ho / rows per strip)
+  int items;   // strips in the whole problem, N * G * S
+  FastDiv divS, divG;
 };
 
 // HardSwish(ReLU(v)) = r * clamp((r + 3) / 6, 0, 1) with r = max(v, 0).  For
@@ -61,41 +89,19 @@ __device__ __forceinline__ float relu_hswish(float v) {
   return fmaxf(v * gate, 0.0f);
 }
 
-// Input rows of one tile: flat output pixels [q0, q0 + TILE) need input rows
-// r = n * H + h from r_first to r_first + R - 1 of all 8 channels.
-struct TileRows {
-  int q0, r_first, R;
+struct Strip {
+  int n, r0, c0;
 };
 
-// Staged row `row` = rr * 8 + ci  <->  input row r_first + rr of channel ci.
-struct Conv2dSrc {
-  const float *x;
-  int H, W, r_first;
-  FastDiv divH;
-  __device__ __forceinline__ const float *operator()(int row) const {
-    const int ci = row & (CI - 1), rr = row >> 3;
-    const int r = r_first + rr, n = fdiv(r, divH), hh = r - n * H;
-    return x + (((size_t)n * CI + ci) * H + hh) * W;
-  }
-};
-struct Conv2dDst {
-  float *lds;
-  int chstride, W;
-  __device__ __forceinline__ float *operator()(int row) const {
-    return lds + (row & (CI - 1)) * chstride + (row >> 3) * W;
-  }
-};
-
-// MT_WAVE: 16-pixel blocks per wave per tile (tile = 16 * MT_WAVE * WAVES pixels).
-// VLOAD: W % 4 == 0 and x 16-byte aligned (16-byte row loads).
+// VLOAD: W % 4 == 0 and x 16-byte aligned (16-byte window loads).
 // VSTORE: P % 4 == 0 and y 16-byte aligned (16-byte result stores).
-// KPRE: staged row passes held in registers while the previous tile computes.
-template <int MT_WAVE, bool VLOAD, bool VSTORE, int KPRE>
+template <class GEO, bool VLOAD, bool VSTORE>
 __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dArgs a) {
-  constexpr int TILE = 16 * MT_WAVE * WAVES;
+  constexpr int RB = GEO::RB, CB = GEO::CB, MT = GEO::MT, SW = GEO::SW, XW = GEO::XW,
+                XQ = GEO::XQ, ROWS = GEO::ROWS, CS = GEO::CS, WIN = GEO::WIN;
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  float *ws = lds;              // weights in B-operand order, WS_FLOATS
-  float *xs = lds + WS_FLOATS;  // input rows, 8 channel planes of chstride floats
+  float *ws = lds;                                  // weights, WS_FLOATS
+  float *win = lds + WS_FLOATS + (threadIdx.x >> 6) * WIN;  // this wave's window
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
 
@@ -109,134 +115,173 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   float bias[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
+  __syncthreads();  // the only workgroup barrier: waves are independent from here on
 
-  // Tiles are dealt round-robin, so the workgroups running at any moment
-  // write neighbouring stretches of the same output channel planes.  The
-  // hardware hands workgroups to the 8 XCDs in turn (b -> XCD b % 8); the
-  // remap gives each XCD a contiguous block of each round's tiles, so one
-  // L2 collects long runs of every plane.  (gridDim.x is a multiple of 8.)
+  // The hardware hands workgroups to the 8 XCDs in turn (b -> XCD b % 8); the
+  // remap gives each XCD a contiguous block of each round's strips, so one L2
+  // collects long runs of every output plane.  (gridDim.x is a multiple of 8.)
   const int per_xcd = gridDim.x >> 3;
-  const int t_begin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3), t_step = gridDim.x;
-  if (t_begin >= a.ntiles) return;
+  const int wg = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int step = gridDim.x * WAVES;
+  // The strip index is the same for every lane of the wave: keep it scalar.
+  // Rounds are workgroup-uniform: round k gives wave w strip
+  // wg * WAVES + k * step + w, and a wave whose strip is past the end idles
+  // through the round, so every wave meets the same barriers.
+  int first = wg * WAVES;
+  if (first >= a.items) return;
+  int item = __builtin_amdgcn_readfirstlane(first + wave);
+  bool valid = item < a.items;
+  if (!valid) item = a.items - 1;
 
-  auto rows_of = [&](int t) {
-    TileRows tr;
-    tr.q0 = t * TILE;
-    const int qlast = min(tr.q0 + TILE, a.Q) - 1;
-    const int n0 = fdiv(tr.q0, a.divP), n1 = fdiv(qlast, a.divP);
-    tr.r_first = n0 * a.H + fdiv(tr.q0 - n0 * a.P, a.divWo);
-    tr.R = n1 * a.H + fdiv(qlast - n1 * a.P, a.divWo) + (KS - 1) - tr.r_first + 1;
-    return tr;
+  auto decode = [&](int i) {
+    const int t = fdiv(i, a.divS), k = i - t * a.S;
+    const int n = fdiv(t, a.divG), rg = t - n * a.G;
+    return Strip{n, rg * RB, k * SW};
   };
-  auto src_of = [&](const TileRows &tr) { return Conv2dSrc{a.x, a.H, a.W, tr.r_first, a.divH}; };
-  auto dst_of = [&](const TileRows &) { return Conv2dDst{xs, a.chstride, a.W}; };
 
-  RowStage<KPRE, VLOAD, THREADS> stage;
-  stage.init(a.W, tid);
-  TileRows cur = rows_of(t_begin);
-  stage.load(CI * cur.R, src_of(cur));
-  stage.store(CI * cur.R, src_of(cur), dst_of(cur));
-  __syncthreads();
-
-  for (int t = t_begin; t < a.ntiles; t += t_step) {
-    const bool more = t + t_step < a.ntiles;
-    TileRows nxt = cur;
-    if (more) {
-      nxt = rows_of(t + t_step);
-      stage.load(CI * nxt.R, src_of(nxt));  // in flight during this tile's MFMAs
+  // Window staging.  Element e of a window is (channel, row, column) with the
+  // column fastest; VLOAD moves quads, otherwise single floats.  Positions
+  // outside the image (left of column 0, right of W - 1, below row H - 1)
+  // are staged as zeros; only masked outputs read them.
+  constexpr int UNITS = VLOAD ? CI * ROWS * XQ : CI * ROWS * XW;
+  constexpr int PER_LANE = (UNITS + 63) / 64;
+  v4f pre[VLOAD ? PER_LANE : 1];
+  float pres[VLOAD ? 1 : PER_LANE];
+  // One image is less than 2^31 floats, so in-image offsets are 32-bit.
+  auto load = [&](const Strip &s) {
+    const float *xs = a.x + (size_t)s.n * CI * a.H * a.W + s.r0 * a.W + s.c0;
+#pragma unroll
+    for (int f = 0; f < PER_LANE; ++f) {
+      const int e = lane + 64 * f;
+      if (e < UNITS) {
+        const int per_row = VLOAD ? XQ : XW;
+        const int cq = e % per_row, rc = e / per_row, row = rc % ROWS, ch = rc / ROWS;
+        const int dc = (VLOAD ? 4 * cq : cq) - 4;
+        const bool ok = s.r0 + row < a.H && s.c0 + dc >= 0 && s.c0 + dc < a.W;
+        const float *p = xs + (ok ? (ch * a.H + row) * a.W + dc : 0);
+        if (VLOAD)
+          pre[f] = ok ? *reinterpret_cast<const v4f *>(p) : splat4(0.0f);
+        else
+          pres[f] = ok ? *p : 0.0f;
+      }
     }
-    const int q0 = cur.q0, r_first = cur.r_first;
-
-#pragma unroll 1
-    for (int mb = 0; mb < MT_WAVE; mb += MT_BATCH) {
-      // Compiler-only fence: keeps the per-step weight reads inside the loop
-      // instead of hoisting all 18 of them (72 VGPRs) out of it.
-      asm volatile("" ::: "memory");
-      // The waves' blocks interleave: together they cover one contiguous run
-      // of 16 * MT_BATCH * WAVES pixels per round.
-      const int blk0 = (mb / MT_BATCH * WAVES + wave) * MT_BATCH;
-      int base[MT_BATCH];
+  };
+  auto put = [&]() {
 #pragma unroll
-      for (int j = 0; j < MT_BATCH; ++j) {
-        int q = q0 + 16 * (blk0 + j) + col;
-        q = min(q, a.Q - 1);  // lanes past the end read a valid pixel; their results are dropped
-        const int n = fdiv(q, a.divP), p = q - n * a.P, h = fdiv(p, a.divWo), w = p - h * a.Wo;
-        base[j] = g * a.chstride + (n * a.H + h - r_first) * a.W + w;
+    for (int f = 0; f < PER_LANE; ++f) {
+      const int e = lane + 64 * f;
+      if (e < UNITS) {
+        const int per_row = VLOAD ? XQ : XW;
+        const int cq = e % per_row, rc = e / per_row, row = rc % ROWS, ch = rc / ROWS;
+        float *d = win + ch * CS + row * XW + (VLOAD ? 4 * cq : cq);
+        if (VLOAD)
+          *reinterpret_cast<v4f *>(d) = pre[f];
+        else
+          *d = pres[f];
       }
-      v4f acc[MT_BATCH][NT];
+    }
+  };
+
+  Strip cur = decode(item);
+  load(cur);
+  put();
+
+  for (;;) {
+    const bool more = first + step < a.items;  // workgroup-uniform
+    int next = __builtin_amdgcn_readfirstlane(first + step + wave);
+    const bool next_valid = next < a.items;
+    if (!next_valid) next = a.items - 1;
+    // The last strip reloads itself: loads and LDS writes stay unconditional,
+    // so the compiler's wait counts never hold a later load behind a store.
+    const Strip nxt = more ? decode(next) : cur;
+    load(nxt);  // in flight during this strip's MFMAs
+
+    // Block (jr, jc) covers output row r0 + jr, columns
+    // [c0 + 16 jc - sh, c0 + 16 jc - sh + 16) with sh = (row offset) mod 4, so
+    // its stores are 16-byte aligned.
+    int sh[RB], base[MT];
 #pragma unroll
-      for (int j = 0; j < MT_BATCH; ++j)
+    for (int jr = 0; jr < RB; ++jr) {
+      const int r = cur.r0 + jr;
+      sh[jr] = VSTORE ? (((r & 3) * (a.Wo & 3)) & 3) : 0;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[j][nt] = splat4(bias[nt]);
+      for (int jc = 0; jc < CB; ++jc) base[jr * CB + jc] = g * CS + jr * XW + 16 * jc + col + 4 - sh[jr];
+    }
+    v4f acc[MT][NT];
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[j][nt] = splat4(bias[nt]);
 
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const int tap = s % TAPS;
-        const int off = (s / TAPS) * 4 * a.chstride + (tap / KS) * a.W + (tap % KS);
-        const v4f bv = *reinterpret_cast<const v4f *>(&ws[(s * 64 + lane) * NT]);
-        float av[MT_BATCH];
+    for (int s = 0; s < KSTEPS; ++s) {
+      const int tap = s % TAPS;
+      const int off = (s / TAPS) * 4 * CS + (tap / KS) * XW + (tap % KS);
+      const v4f bv = *reinterpret_cast<const v4f *>(&ws[(s * 64 + lane) * NT]);
+      float av[MT];
 #pragma unroll
-        for (int j = 0; j < MT_BATCH; ++j) av[j] = xs[base[j] + off];
+      for (int j = 0; j < MT; ++j) av[j] = win[base[j] + off];
 #pragma unroll
-        for (int j = 0; j < MT_BATCH; ++j) {
-          acc[j][0] = mfma16x16x4(av[j], bv.x, acc[j][0]);
-          acc[j][1] = mfma16x16x4(av[j], bv.y, acc[j][1]);
-          acc[j][2] = mfma16x16x4(av[j], bv.z, acc[j][2]);
-          acc[j][3] = mfma16x16x4(av[j], bv.w, acc[j][3]);
-        }
+      for (int j = 0; j < MT; ++j) {
+        acc[j][0] = mfma16x16x4(av[j], bv.x, acc[j][0]);
+        acc[j][1] = mfma16x16x4(av[j], bv.y, acc[j][1]);
+        acc[j][2] = mfma16x16x4(av[j], bv.z, acc[j][2]);
+        acc[j][3] = mfma16x16x4(av[j], bv.w, acc[j][3]);
+      }
+    }
+
+    // The window has been read (the MFMAs above consumed every value), so the
+    // next strip's window may overwrite it; this wave's LDS operations run in
+    // program order.
+    asm volatile("" ::: "memory");
+    put();
+
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[j][nt].x = relu_hswish(acc[j][nt].x);
+        acc[j][nt].y = relu_hswish(acc[j][nt].y);
+        acc[j][nt].z = relu_hswish(acc[j][nt].z);
+        acc[j][nt].w = relu_hswish(acc[j][nt].w);
       }
 
 #pragma unroll
-      for (int j = 0; j < MT_BATCH; ++j) {
-        const int qq = q0 + 16 * (blk0 + j) + 4 * g;  // this lane's first pixel
-        if (qq >= a.Q) continue;
-        if (VSTORE) {
-          // P % 4 == 0 and Q % 4 == 0: the four pixels are in one plane and all valid.
-          const int n = fdiv(qq, a.divP), p = qq - n * a.P;
-          float *dst = a.y + (size_t)n * CO * a.P + p;
+    for (int j = 0; j < MT; ++j) {
+      const int jr = j / CB, jc = j % CB, r = cur.r0 + jr;
+      if (r >= a.Ho || !valid) break;
+      const int cb = cur.c0 + 16 * jc - sh[jr] + 4 * g;  // this lane's first output column
+      float *dst = a.y + (size_t)cur.n * CO * a.P + (size_t)r * a.Wo + cb;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            v4f v = acc[j][nt];
-            v.x = relu_hswish(v.x);
-            v.y = relu_hswish(v.y);
-            v.z = relu_hswish(v.z);
-            v.w = relu_hswish(v.w);
-            store4(dst + (size_t)(16 * nt + col) * a.P, v);
-          }
+      for (int nt = 0; nt < NT; ++nt) {
+        const v4f v = acc[j][nt];
+        float *d = dst + (size_t)(16 * nt + col) * a.P;
+        if (VSTORE && cb >= 0 && cb + 3 < a.Wo) {
+          store4(d, v);
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int qr = qq + r;
-            if (qr >= a.Q) break;
-            const int n = fdiv(qr, a.divP), p = qr - n * a.P;
-            float *dst = a.y + (size_t)n * CO * a.P + p;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              dst[(size_t)(16 * nt + col) * a.P] = relu_hswish(acc[j][nt][r]);
-          }
+          for (int e = 0; e < 4; ++e)
+            if (cb + e >= 0 && cb + e < a.Wo) d[e] = v[e];
         }
       }
     }
 
-    if (more) {
-      __syncthreads();  // every wave is done reading this tile's rows
-      stage.store(CI * nxt.R, src_of(nxt), dst_of(nxt));
-      __syncthreads();
-      cur = nxt;
-    }
+    if (!more) break;
+    __syncthreads();  // the workgroup's waves start the next round together
+    cur = nxt;
+    item = next;
+    valid = next_valid;
+    first += step;
   }
 }
 
-template <int MT_WAVE, bool VL, bool VS>
-int launch_instance(const Conv2dArgs &a, int R_max, hipStream_t stream) {
-  constexpr int TILE = 16 * MT_WAVE * WAVES;
-  (void)TILE;
+template <class GEO, bool VL, bool VS>
+int launch_instance(const Conv2dArgs &a, hipStream_t stream) {
   DeviceInfo dev;
   if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
-  const size_t lds_bytes = ((size_t)WS_FLOATS + (size_t)CI * a.chstride) * sizeof(float);
-  (void)R_max;
+  const size_t lds_bytes = ((size_t)WS_FLOATS + (size_t)WAVES * GEO::WIN) * sizeof(float);
   if (lds_bytes > dev.lds_per_block) return CCE_ERR_UNSUPPORTED;
-  auto kern = conv2d_relu_hswish_kernel<MT_WAVE, VL, VS, kPrefetchPasses>;
+  auto kern = conv2d_relu_hswish_kernel<GEO, VL, VS>;
   if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds_bytes) != hipSuccess)
     return CCE_ERR_LAUNCH;
@@ -245,8 +290,9 @@ int launch_instance(const Conv2dArgs &a, int R_max, hipStream_t stream) {
       per_cu < 1)
     per_cu = 1;
   int grid = dev.num_cus * per_cu;
-  if (grid > a.ntiles) grid = a.ntiles;
-  grid = (grid + 7) & ~7;  // the XCD remap needs a multiple of 8; surplus workgroups exit
+  const int needed = (a.items + WAVES - 1) / WAVES;
+  if (grid > needed) grid = needed;
+  grid = (grid + 7) & ~7;  // the XCD remap needs a multiple of 8; surplus waves exit
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds_bytes, stream, a);
   return launch_status();
 }
@@ -255,6 +301,10 @@ int launch_instance(const Conv2dArgs &a, int R_max, hipStream_t stream) {
 
 int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
                               int H, int W, hipStream_t stream) {
+  // Strips of 2 rows x 16 columns.  Measured on MI355X at N = 128 (ms):
+  // 2 x 16: 0.199, 1 x 16: 0.204, 1 x 32: 0.211, 3 x 16: 0.294 (spills);
+  // 16-wave workgroups 0.195 against 0.199 for 8-wave ones.
+  using Geo = StripGeo<2, 1>;
   Conv2dArgs a;
   a.x = x;
   a.w = w;
@@ -262,40 +312,29 @@ int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, fl
   a.y = y;
   a.H = H;
   a.W = W;
+  a.Ho = H - (KS - 1);
   a.Wo = W - (KS - 1);
-  const int Ho = H - (KS - 1);
-  a.P = Ho * a.Wo;
-  a.Q = N * a.P;
-  a.divP = make_fastdiv((uint32_t)a.P);
-  a.divWo = make_fastdiv((uint32_t)a.Wo);
-  a.divH = make_fastdiv((uint32_t)H);
-
-  DeviceInfo dev;
-  if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
-  // Tiles of 256 pixels (8 waves x 2 blocks of 16).  Measured on MI355X at
-  // N = 128: 256-pixel tiles 0.222 ms, 512: 0.227 ms, 1024: 0.234 ms -- with
-  // round-robin tiles, smaller tiles keep the concurrently written stretches
-  // of each output plane closer together.
-  const int tile = 256;
-  a.ntiles = (a.Q + tile - 1) / tile;
-
-  // Upper bound on the input rows one tile touches: output rows spanned plus
-  // (k - 1) halo rows for every image the tile reaches into.
-  const int rows_spanned = (tile - 1 + a.Wo - 1) / a.Wo + 1;
-  const int images_spanned = (tile - 1 + a.P - 1) / a.P + 1;
-  int R_max = rows_spanned + (KS - 1) * images_spanned;
-  if (R_max > N * H) R_max = N * H;
-  // Channel planes padded so the four lane groups (four channels) of a read
-  // start 16 banks apart.
-  int plane = R_max * W;
-  a.chstride = plane + ((16 - plane % 64) + 64) % 64;
+  a.P = a.Ho * a.Wo;
 
   const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
   const bool vs = (a.P % 4 == 0) && ((uintptr_t)y % 16 == 0);
-  if (vl) return vs ? launch_instance<2, true, true>(a, R_max, stream)
-                    : launch_instance<2, true, false>(a, R_max, stream);
-  return vs ? launch_instance<2, false, true>(a, R_max, stream)
-            : launch_instance<2, false, false>(a, R_max, stream);
+  // Largest left shift any row's strips take (0 when stores are scalar).
+  int sh_max = 0;
+  if (vs)
+    for (int r = 0; r < 4 && r < a.Ho; ++r) {
+      const int sh = (r * (a.Wo & 3)) & 3;
+      if (sh > sh_max) sh_max = sh;
+    }
+  a.S = (a.Wo + sh_max + Geo::SW - 1) / Geo::SW;
+  a.G = (a.Ho + Geo::RB - 1) / Geo::RB;
+  const long long items = (long long)N * a.G * a.S;
+  if (items >= (1LL << 31) - (1LL << 24)) return CCE_ERR_TOO_LARGE;
+  a.items = (int)items;
+  a.divS = make_fastdiv((uint32_t)a.S);
+  a.divG = make_fastdiv((uint32_t)a.G);
+
+  if (vl) return vs ? launch_instance<Geo, true, true>(a, stream) : launch_instance<Geo, true, false>(a, stream);
+  return vs ? launch_instance<Geo, false, true>(a, stream) : launch_instance<Geo, false, false>(a, stream);
 }
 
 }  // namespace cce

@@ -70,9 +70,10 @@ int cce_version(void);
  * padding 0, the defaults the page's problem uses), r = max(z, 0),
  * y = r * clamp((r + 3) / 6, 0, 1).
  *
- * Supported: C_in = 8, C_out = 64, k = 3, any N >= 1, H, W >= 3 with the
- * input tile of 8 channel rows fitting in LDS (W <= 1024), N*(H-2)*(W-2)
- * < 2^31.  Anything else returns CCE_ERR_UNSUPPORTED.
+ * Supported: C_in = 8, C_out = 64, k = 3, any N >= 1, H, W >= 3; other
+ * channel counts or kernel sizes return CCE_ERR_UNSUPPORTED.  One input image
+ * (8*H*W floats) and the output pixel count N*(H-2)*(W-2) must stay below
+ * 2^31, else CCE_ERR_TOO_LARGE.
  */
 int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N, int C_in,
                        int H, int W, int C_out, int k, void *stream);

@@ -61,6 +61,18 @@ def test_record_traffic_scales_by_copy_calibration(tmp_path):
     assert r["source_sha256_16"] == bench.source_digest("conv2d_relu_hswish")
     assert "conv3d_lrelu_add_clamp_gelu_n128" not in rec
 
+    # A record from an earlier run survives only while its kernel source is unchanged.
+    prev = {"copy_scale": {"fetch": 2.0, "write": 1.0},
+            "conv3d_lrelu_add_clamp_gelu_n128": {"source_sha256_16": bench.source_digest("conv3d_lrelu_add_clamp_gelu"),
+                                                 "bytes_per_launch": 7},
+            "convT2d_pool_htanh_mean_tanh_n16": {"source_sha256_16": "stale", "bytes_per_launch": 9},
+            "conv2d_relu_hswish_n8": {"source_sha256_16": bench.source_digest("conv2d_relu_hswish"),
+                                      "bytes_per_launch": 5}}
+    rec = bench.record_traffic(tmp_path, mib, prev)
+    assert rec["conv3d_lrelu_add_clamp_gelu_n128"]["bytes_per_launch"] == 7
+    assert "convT2d_pool_htanh_mean_tanh_n16" not in rec
+    assert rec["conv2d_relu_hswish_n8"]["bytes_per_launch"] == r["bytes_per_launch"]
+
 
 def test_bench_refuses_more_than_one_gpu():
     res = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "8"], capture_output=True,

@@ -60,13 +60,16 @@ def sample_indices(total, count, seed):
 # Conv2d + ReLU + HardSwish
 # ---------------------------------------------------------------------------
 
-CONV2D_SMALL = [  # (N, H, W, bias)   covers: tiles, image-crossing tiles, odd sizes, minimum
+CONV2D_SMALL = [  # (N, H, W, bias)   covers: strips, ragged row groups and columns, odd sizes, minimum
     (2, 20, 20, True),
-    (3, 37, 29, True),   # W % 4 != 0, plane % 4 != 0: scalar loads and stores
+    (3, 37, 29, True),   # W % 4 != 0, plane % 4 != 0: scalar loads and stores; odd output height
     (1, 3, 3, True),     # one output pixel
     (5, 128, 128, True),
-    (4, 11, 130, False),  # NULL bias, wide rows
-    (7, 64, 66, True),   # 7 images: tiles straddle image boundaries, ragged last tile
+    (4, 11, 130, False),  # NULL bias, wide rows: 9 strips, the last one ragged
+    (7, 64, 66, True),   # 7 images, output rows of 64 (no strip shift)
+    (2, 6, 7, True),     # odd output width with plane % 4 == 0: strips shifted by 0..3 columns
+    (3, 18, 19, True),   # the same with two strips per row and masked edge lanes
+    (1, 6, 1100, True),  # rows wider than 1024: 69 strips, shifted, 16-byte loads
 ]
 
 
