@@ -5,18 +5,23 @@
 // approximate=False).
 //
 // Design:
-//  * Implicit GEMM on the fp32 matrix cores: M = output voxels, N = output
-//    channels, K = 8 channels x 27 taps = 216.  A tile is one output depth
-//    plane d of one image and TR consecutive output rows (all columns); its
-//    input -- 8 channels x 3 depth planes x (TR + 2) rows x W -- is staged in
-//    LDS once.  Voxels inside the tile are numbered flat (row-major), so a
-//    lane's four result voxels are consecutive in memory.
-//  * Each of the 8 waves owns 16 of the 64 output channels; the matching
-//    216 x 16 weight slice lives in 54 VGPRs per lane for the whole
-//    (persistent) workgroup, which keeps 4 waves per SIMD resident.  The
-//    four waves of a channel split the tile's 16-voxel blocks two ways.  Per
-//    K-step a lane reads one A value from LDS at a lane-independent step
-//    offset (lane group g = input channel within a group of 4).
+//  * Implicit GEMM on the fp32 matrix cores: M = output voxels, N = the 64
+//    output channels, K = 8 channels x 27 taps = 216 (54 K-steps of 4).
+//  * A tile is one output depth plane d of a block of TR output rows and TC
+//    output columns of one image (TC = the whole row when it fits).  Its
+//    input -- 8 channels x 3 depth planes x (TR + 2) rows x (TC + 2) columns
+//    -- comes from a ring of 4 staged input planes in LDS: a workgroup walks
+//    d = 0, 1, 2, ... down one row block, so each tile needs one new plane,
+//    which is loaded into registers during the tile's MFMAs and written to
+//    the ring's free slot after them; one barrier per tile.
+//  * The 216 x 64 weight sits in LDS in B-operand order (55 KB): one 16-byte
+//    read per K-step gives a lane its B values for all four 16-channel blocks,
+//    so each A value read from LDS feeds four MFMAs.  Every wave of the
+//    16-wave workgroup computes two 16-voxel blocks x 64 channels per tile:
+//    eight independent accumulator chains.
+//  * Workgroups take row blocks round-robin (remapped so each XCD gets a
+//    contiguous run): neighbouring row blocks of one image run at the same
+//    time and write neighbouring stretches of every output plane.
 //  * The epilogue (bias as accumulator init, LeakyReLU, add, clamp, GELU with
 //    erf) runs in registers; only the final value is stored.
 #include "cce_device.hpp"
@@ -26,12 +31,13 @@ namespace cce {
 namespace {
 
 constexpr int CI = 8, CO = 64, KS = 3, TAPS = KS * KS * KS;
-constexpr int KSTEPS = (CI / 4) * TAPS;  // 54 steps of 4 taps
-constexpr int CG = 4;                    // channel groups of 16: wave w owns channels 16 (w % 4) ..
-constexpr int MG = 2;                    // voxel groups: wave w takes 16-voxel blocks w / 4, + 2, ...
-constexpr int WAVES = CG * MG, THREADS = 64 * WAVES;
-constexpr int MT_BATCH = 2;
-constexpr int kPrefetchPasses = 3;  // one plane: 8 ch x 10 rows of 64 floats, 32 rows per pass
+constexpr int KSTEPS = (CI / 4) * TAPS;      // 54 steps of 4 taps
+constexpr int NT = CO / 16;                  // 4 channel blocks of 16
+constexpr int WAVES = 16, THREADS = 64 * WAVES;  // one workgroup per CU, 4 waves per SIMD
+constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // 13824 floats (55 KB)
+constexpr int SLOTS = 4;                     // input planes held in LDS
+constexpr int MT = 2;                        // 16-voxel blocks per wave per pass
+constexpr int kPrefetchPasses = 2;           // a plane of 8 x 10 rows of 64 floats takes 2 passes
 
 struct Conv3dArgs {
   const float *__restrict__ x;
@@ -41,177 +47,218 @@ struct Conv3dArgs {
   float *__restrict__ y;
   int D, H, W, Do, Ho, Wo;
   int TR;           // output rows per tile
+  int TC;           // output columns per tile (a multiple of 4, or Wo)
+  int XC;           // staged columns per row in LDS
   int rowtiles;     // ceil(Ho / TR)
-  int ntiles;       // N * Do * rowtiles
-  int chstride;     // floats between channel blocks in LDS
-  int planestride;  // floats between depth planes in LDS, (TR + 2) * W
+  int coltiles;     // ceil(Wo / TC)
+  int nblocks;      // N * rowtiles * coltiles row-column blocks
+  int chstride;     // floats between channels in LDS (SLOTS planes + padding)
+  int planestride;  // floats between ring slots, (TR + 2) * XC
   float slope, lo, hi;
-  FastDiv divDo, divRowtiles, divWo;
+  FastDiv divRowCol, divCol, divTC, divTClast;
 };
 
-// One tile: output depth plane d of image n, output rows h0 .. h0 + rows - 1.
-// Tiles are numbered with d fastest, so a run of consecutive tiles walks down
-// the depth axis of one row block and each step needs one new input plane.
-struct Tile3 {
-  int n, d, h0, rows;
-};
-
-// One input depth plane dd of a row block: staged row `row` = rr * 8 + ci
-// <-> x[n][ci][dd][h0 + rr][:], stored in LDS ring slot dd % 3.
+// One staged input plane dd of a row-column block: staged row `row` =
+// rr * 8 + ci <-> x[n][ci][dd][h0 + rr][c0 ...], stored in ring slot dd % 4.
 struct PlaneSrc {
   const float *x;
-  int D, H, W, n, dd, h0;
+  int D, H, W, n, dd, h0, c0;
   __device__ __forceinline__ const float *operator()(int row) const {
     const int ci = row & (CI - 1), rr = row >> 3;
-    return x + ((((size_t)n * CI + ci) * D + dd) * H + (h0 + rr)) * W;
+    return x + ((((size_t)n * CI + ci) * D + dd) * H + (h0 + rr)) * W + c0;
   }
 };
 struct PlaneDst {
-  float *lds;
-  int chstride, slot_off, W;
+  float *xs;
+  int chstride, slot_off, XC;
   __device__ __forceinline__ float *operator()(int row) const {
-    return lds + (row & (CI - 1)) * chstride + slot_off + (row >> 3) * W;
+    return xs + (row & (CI - 1)) * chstride + slot_off + (row >> 3) * XC;
   }
 };
 
-template <bool VLOAD, bool VSTORE, bool SERIES, int KPRE>
+// LDS floats for tiles of tr rows whose staged rows hold xc floats: ring
+// slots of (tr + 2) xc floats, channels 16 mod 64 floats apart so the four
+// lane groups of an A read (four channels) start on four different quarters
+// of the 64 LDS banks.
+constexpr int plane_floats(int tr, int xc) { return (tr + KS - 1) * xc; }
+constexpr int chan_floats(int tr, int xc) {
+  return SLOTS * plane_floats(tr, xc) + ((16 - (SLOTS * plane_floats(tr, xc)) % 64) + 64) % 64;
+}
+
+// FIXED_XC / FIXED_TR: staged row length and tile rows known at compile time
+// (then every per-step LDS offset is an immediate); 0 = taken from the args.
+// VLOAD: W % 4 == 0 and x 16-byte aligned (16-byte plane loads).
+// VSTORE: every lane's four voxels are consecutive and 16-byte aligned in y.
+// SERIES: the clamp bounds lie in [-1, 1] (series GELU).
+template <int FIXED_XC, int FIXED_TR, bool VLOAD, bool VSTORE, bool SERIES>
 __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel(Conv3dArgs a) {
-  extern __shared__ float lds[];
+  const int XC = FIXED_XC ? FIXED_XC : a.XC;
+  const int TR = FIXED_TR ? FIXED_TR : a.TR;
+  const int chstride = FIXED_XC ? chan_floats(FIXED_TR, FIXED_XC) : a.chstride;
+  const int planestride = FIXED_XC ? plane_floats(FIXED_TR, FIXED_XC) : a.planestride;
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  float *ws = lds;              // weights, B-operand order
+  float *xs = lds + WS_FLOATS;  // ring of input planes
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
-  const int o = 16 * (wave % CG) + col;  // this lane's output channel
-  const int mg = wave / CG;              // which interleaved set of 16-voxel blocks
 
-  // B operand of every K-step for this wave's 16 channels (54 VGPRs).
-  float wr[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) wr[s] = a.w[(o * CI + 4 * (s / TAPS) + g) * TAPS + (s % TAPS)];
-  const float bias = a.b ? a.b[o] : 0.0f;
-  const float sadd = a.s[o];
-  const size_t vol = (size_t)a.Do * a.Ho * a.Wo;  // output voxels per (n, channel)
+  // ws[s][lane][nt] = w[16 nt + lane % 16][4 (s / 27) + lane / 16][tap s % 27].
+  for (int e = tid; e < WS_FLOATS; e += THREADS) {
+    const int nt = e & 3, ln = (e >> 2) & 63, st = e >> 8;
+    const int o = 16 * nt + (ln & 15), ci = 4 * (st / TAPS) + (ln >> 4);
+    ws[e] = a.w[(o * CI + ci) * TAPS + (st % TAPS)];
+  }
+  // Bias and the added per-channel term, read from LDS when needed (fewer
+  // live registers): ep[c] = b[c], ep[64 + c] = s[c].
+  float *ep = xs + CI * chstride;
+  if (tid < CO) {
+    ep[tid] = a.b ? a.b[tid] : 0.0f;
+    ep[CO + tid] = a.s[tid];
+  }
+  // Output voxels per (n, channel); one image's output is below 2^31 floats,
+  // so offsets within it are 32-bit.
+  const int vol = a.Do * a.Ho * a.Wo;
 
-  const int t_begin = (int)(((long long)blockIdx.x * a.ntiles) / gridDim.x);
-  const int t_end = (int)(((long long)(blockIdx.x + 1) * a.ntiles) / gridDim.x);
-  if (t_begin >= t_end) return;
+  // Row-column blocks round-robin; the hardware hands workgroups to the 8
+  // XCDs in turn, and the remap gives each XCD consecutive blocks.
+  // (gridDim.x is a multiple of 8.)
+  const int per_xcd = gridDim.x >> 3;
+  const int vb = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
 
-  auto tile_of = [&](int t) {
-    Tile3 tl;
-    const int q = fdiv(t, a.divDo);
-    tl.d = t - q * a.Do;
-    tl.n = fdiv(q, a.divRowtiles);
-    const int rt = q - tl.n * a.rowtiles;
-    tl.h0 = rt * a.TR;
-    tl.rows = min(a.TR, a.Ho - tl.h0);
-    return tl;
-  };
-  auto src_of = [&](const Tile3 &tl, int dd) {
-    return PlaneSrc{a.x, a.D, a.H, a.W, tl.n, dd, tl.h0};
-  };
-  auto dst_of = [&](const Tile3 &, int dd) {
-    return PlaneDst{lds, a.chstride, (dd % KS) * a.planestride, a.W};
-  };
-  auto nrows = [&](const Tile3 &tl) { return CI * (tl.rows + (KS - 1)); };
+  RowStage<kPrefetchPasses, VLOAD, THREADS> stage;
+  __syncthreads();  // weights in place
 
-  // Registers carry one input plane ahead: plane d + 3 while tile d computes,
-  // or the first plane of a new row block (its other two are copied directly).
-  RowStage<KPRE, VLOAD, THREADS> stage;
-  stage.init(a.W, tid);
-  Tile3 cur = tile_of(t_begin);
-  stage.load(nrows(cur), src_of(cur, cur.d));
-  stage.store(nrows(cur), src_of(cur, cur.d), dst_of(cur, cur.d));
-  stage.load(nrows(cur), src_of(cur, cur.d + 1));
-  stage.store(nrows(cur), src_of(cur, cur.d + 1), dst_of(cur, cur.d + 1));
-  stage.load(nrows(cur), src_of(cur, cur.d + 2));
-  stage.store(nrows(cur), src_of(cur, cur.d + 2), dst_of(cur, cur.d + 2));
-  __syncthreads();
+  for (int rb = vb; rb < a.nblocks; rb += gridDim.x) {
+    const int n = fdiv(rb, a.divRowCol), rc = rb - n * (a.rowtiles * a.coltiles);
+    const int rt = fdiv(rc, a.divCol), ct = rc - rt * a.coltiles;
+    const int h0 = rt * TR, rows = min(TR, a.Ho - h0);
+    const int c0 = ct * a.TC, cols = min(a.TC, a.Wo - c0);
+    const bool last_col = ct == a.coltiles - 1;
+    const int nr = CI * (rows + KS - 1);                // staged rows per plane
+    const int len = min(XC, a.W - c0);                // staged floats per row
+    const bool contig = a.coltiles == 1;                // the tile spans whole output rows
+    const int V = rows * cols, MTT = (V + 15) >> 4;     // voxels and 16-voxel blocks
+    stage.init(len, tid);
+    auto src_of = [&](int dd) { return PlaneSrc{a.x, a.D, a.H, a.W, n, dd, h0, c0}; };
+    auto dst_of = [&](int dd) { return PlaneDst{xs, chstride, (dd % SLOTS) * planestride, XC}; };
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const bool more = t + 1 < t_end;
-    Tile3 nxt = cur;
-    bool fresh = false;  // next tile starts a new row block (needs three planes)
-    if (more) {
-      nxt = tile_of(t + 1);
-      fresh = nxt.d == 0;
-      stage.load(nrows(nxt), src_of(nxt, fresh ? 0 : nxt.d + 2));
+    // Planes 0, 1, 2 of this block (every wave is past the previous block's
+    // last barrier, so all slots are free).
+#pragma unroll 1
+    for (int dd = 0; dd < KS; ++dd) {
+      stage.load(nr, src_of(dd));
+      stage.store(nr, src_of(dd), dst_of(dd));
     }
-    const int V = cur.rows * a.Wo;  // voxels in this tile
-    const int MTT = (V + 15) >> 4;
-    float *ybase = a.y + ((size_t)cur.n * CO) * vol + (size_t)cur.d * a.Ho * a.Wo +
-                   (size_t)cur.h0 * a.Wo;
-    // LDS offsets of input planes d, d + 1, d + 2 in the ring.
-    const int so0 = (cur.d % KS) * a.planestride;
-    const int so1 = ((cur.d + 1) % KS) * a.planestride;
-    const int so2 = ((cur.d + 2) % KS) * a.planestride;
+    __syncthreads();
 
 #pragma unroll 1
-    for (int mb = mg * MT_BATCH; mb < MTT; mb += MG * MT_BATCH) {
-      int base[MT_BATCH][KS];
+    for (int d = 0; d < a.Do; ++d) {
+      const bool more = d + KS < a.D;  // plane d + 3 exists
+      if (more) stage.load(nr, src_of(d + KS));  // in flight during this tile's MFMAs
+      const int so0 = (d % SLOTS) * planestride;
+      const int so1 = ((d + 1) % SLOTS) * planestride;
+      const int so2 = ((d + 2) % SLOTS) * planestride;
+      float *ytile = a.y + (size_t)n * CO * vol + (size_t)d * a.Ho * a.Wo;  // uniform
+
+#pragma unroll 1
+      for (int mb_iv = MT * wave; mb_iv < MTT; mb_iv += MT * WAVES) {
+        // Compiler-only fences: the first keeps the per-step weight reads
+        // inside the loop instead of hoisting all 54 of them (216 VGPRs) out
+        // of it; the second hides the block index from strength reduction,
+        // which would otherwise keep eight 64-bit store pointers live.
+        asm volatile("" ::: "memory");
+        int mb = mb_iv;
+        asm volatile("" : "+v"(mb));
+        int base[MT][KS];
 #pragma unroll
-      for (int j = 0; j < MT_BATCH; ++j) {
-        const int v = min(16 * (mb + j) + col, V - 1);
-        const int hl = fdiv(v, a.divWo), w = v - hl * a.Wo;
-        const int b0 = g * a.chstride + hl * a.W + w;
-        base[j][0] = b0 + so0;
-        base[j][1] = b0 + so1;
-        base[j][2] = b0 + so2;
-      }
-      v4f acc[MT_BATCH];
+        for (int j = 0; j < MT; ++j) {
+          const int v = min(16 * (mb + j) + col, V - 1);
+          const int hl = fdiv(v, last_col ? a.divTClast : a.divTC), wl = v - hl * cols;
+          const int b0 = g * chstride + hl * XC + wl;
+          base[j][0] = b0 + so0;
+          base[j][1] = b0 + so1;
+          base[j][2] = b0 + so2;
+        }
+        v4f acc[MT][NT];
 #pragma unroll
-      for (int j = 0; j < MT_BATCH; ++j) acc[j] = splat4(bias);
+        for (int nt = 0; nt < NT; ++nt) {
+          const float bias = ep[16 * nt + col];
+#pragma unroll
+          for (int j = 0; j < MT; ++j) acc[j][nt] = splat4(bias);
+        }
 
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const int tt = s % TAPS, kd = tt / 9, kh = (tt / 3) % 3, kw = tt % 3;
-        const int off = (s / TAPS) * 4 * a.chstride + kh * a.W + kw;
-        float av[MT_BATCH];
+        for (int s = 0; s < KSTEPS; ++s) {
+          const int tt = s % TAPS, kd = tt / 9, kh = (tt / 3) % 3, kw = tt % 3;
+          const int off = (s / TAPS) * 4 * chstride + kh * XC + kw;
+          const v4f bv = *reinterpret_cast<const v4f *>(&ws[(s * 64 + lane) * NT]);
+          float av[MT];
 #pragma unroll
-        for (int j = 0; j < MT_BATCH; ++j) av[j] = lds[base[j][kd] + off];
+          for (int j = 0; j < MT; ++j) av[j] = xs[base[j][kd] + off];
 #pragma unroll
-        for (int j = 0; j < MT_BATCH; ++j) acc[j] = mfma16x16x4(av[j], wr[s], acc[j]);
-      }
+          for (int j = 0; j < MT; ++j) {
+            acc[j][0] = mfma16x16x4(av[j], bv.x, acc[j][0]);
+            acc[j][1] = mfma16x16x4(av[j], bv.y, acc[j][1]);
+            acc[j][2] = mfma16x16x4(av[j], bv.z, acc[j][2]);
+            acc[j][3] = mfma16x16x4(av[j], bv.w, acc[j][3]);
+          }
+        }
 
 #pragma unroll
-      for (int j = 0; j < MT_BATCH; ++j) {
-        const int v0 = 16 * (mb + j) + 4 * g;
-        if (v0 >= V) continue;
-        float *dst = ybase + (size_t)o * vol + v0;
-        v4f r = acc[j];
-        r.x = lrelu_add_clamp_gelu_value<SERIES>(r.x, sadd, a.slope, a.lo, a.hi);
-        r.y = lrelu_add_clamp_gelu_value<SERIES>(r.y, sadd, a.slope, a.lo, a.hi);
-        r.z = lrelu_add_clamp_gelu_value<SERIES>(r.z, sadd, a.slope, a.lo, a.hi);
-        r.w = lrelu_add_clamp_gelu_value<SERIES>(r.w, sadd, a.slope, a.lo, a.hi);
-        if (VSTORE && v0 + 3 < V) {
-          store4(dst, r);
-        } else {
-          dst[0] = r.x;
-          if (v0 + 1 < V) dst[1] = r.y;
-          if (v0 + 2 < V) dst[2] = r.z;
-          if (v0 + 3 < V) dst[3] = r.w;
+        for (int j = 0; j < MT; ++j) {
+          const int v0 = 16 * (mb + j) + 4 * g;  // this lane's first voxel in the tile
+          if (v0 >= V) continue;
+          // Output offset of voxel v0 within the (n, channel, d) plane.
+          int off0, run;  // run: voxels from v0 that are consecutive in memory
+          if (contig) {
+            off0 = h0 * a.Wo + v0;
+            run = V - v0;
+          } else {
+            const int hl = fdiv(v0, last_col ? a.divTClast : a.divTC), wl = v0 - hl * cols;
+            off0 = (h0 + hl) * a.Wo + c0 + wl;
+            run = cols - wl;
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const float sadd = ep[CO + 16 * nt + col];
+            v4f r = acc[j][nt];
+            r.x = lrelu_add_clamp_gelu_value<SERIES>(r.x, sadd, a.slope, a.lo, a.hi);
+            r.y = lrelu_add_clamp_gelu_value<SERIES>(r.y, sadd, a.slope, a.lo, a.hi);
+            r.z = lrelu_add_clamp_gelu_value<SERIES>(r.z, sadd, a.slope, a.lo, a.hi);
+            r.w = lrelu_add_clamp_gelu_value<SERIES>(r.w, sadd, a.slope, a.lo, a.hi);
+            float *dst = ytile + ((16 * nt + col) * vol + off0);
+            if (VSTORE && run >= 4) {
+              store4(dst, r);
+            } else {
+              // Voxels past the end of a row segment continue on the next row.
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int ve = v0 + e;
+                if (ve >= V) break;
+                if (contig) {
+                  dst[e] = r[e];
+                } else {
+                  const int hl = fdiv(ve, last_col ? a.divTClast : a.divTC), wl = ve - hl * cols;
+                  ytile[(16 * nt + col) * vol + (h0 + hl) * a.Wo + c0 + wl] = r[e];
+                }
+              }
+            }
+          }
         }
       }
-    }
 
-    if (more) {
-      __syncthreads();  // every wave is done reading plane d (its slot is reused)
-      if (fresh) {
-        stage.store(nrows(nxt), src_of(nxt, 0), dst_of(nxt, 0));
-        stage.load(nrows(nxt), src_of(nxt, 1));
-        stage.store(nrows(nxt), src_of(nxt, 1), dst_of(nxt, 1));
-        stage.load(nrows(nxt), src_of(nxt, 2));
-        stage.store(nrows(nxt), src_of(nxt, 2), dst_of(nxt, 2));
-      } else {
-        stage.store(nrows(nxt), src_of(nxt, nxt.d + 2), dst_of(nxt, nxt.d + 2));
-      }
-      __syncthreads();
-      cur = nxt;
+      // Plane d + 3 goes to slot (d + 3) % 4, last read by tile d - 1, which
+      // every wave finished before the previous barrier.
+      if (more) stage.store(nr, src_of(d + KS), dst_of(d + KS));
+      __syncthreads();  // plane d + 3 visible; plane d free
     }
   }
 }
 
-template <bool VL, bool VS, bool SER>
+template <int FXC, int FTR, bool VL, bool VS, bool SER>
 int launch_instance(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev,
                     hipStream_t stream) {
-  auto kern = conv3d_lrelu_add_clamp_gelu_kernel<VL, VS, SER, kPrefetchPasses>;
+  auto kern = conv3d_lrelu_add_clamp_gelu_kernel<FXC, FTR, VL, VS, SER>;
   if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds_bytes) != hipSuccess)
     return CCE_ERR_LAUNCH;
@@ -220,7 +267,8 @@ int launch_instance(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev
       per_cu < 1)
     per_cu = 1;
   int grid = dev.num_cus * per_cu;
-  if (grid > a.ntiles) grid = a.ntiles;
+  if (grid > a.nblocks) grid = a.nblocks;
+  grid = (grid + 7) & ~7;  // the XCD remap needs a multiple of 8; surplus workgroups exit
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds_bytes, stream, a);
   return launch_status();
 }
@@ -229,8 +277,19 @@ template <bool VL, bool VS>
 int launch_series(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev,
                   hipStream_t stream) {
   const bool series = a.lo >= -1.0f && a.hi <= 1.0f;
-  return series ? launch_instance<VL, VS, true>(a, lds_bytes, dev, stream)
-                : launch_instance<VL, VS, false>(a, lds_bytes, dev, stream);
+  // 64-float staged rows in 8-row tiles (W = 64, as in the page's workload)
+  // get their own instance with compile-time LDS offsets.
+  if (a.XC == 64 && a.TR == 8)
+    return series ? launch_instance<64, 8, VL, VS, true>(a, lds_bytes, dev, stream)
+                  : launch_instance<64, 8, VL, VS, false>(a, lds_bytes, dev, stream);
+  return series ? launch_instance<0, 0, VL, VS, true>(a, lds_bytes, dev, stream)
+                : launch_instance<0, 0, VL, VS, false>(a, lds_bytes, dev, stream);
+}
+
+size_t ring_floats(int tr, int xc, int *planestride, int *chstride) {
+  *planestride = plane_floats(tr, xc);
+  *chstride = chan_floats(tr, xc);
+  return (size_t)CI * *chstride;
 }
 
 }  // namespace
@@ -255,32 +314,55 @@ int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const flo
   a.slope = slope;
   a.lo = lo;
   a.hi = hi;
-  // Largest row count per tile (8, 4, 2 or 1) whose input slab fits in LDS.
-  size_t lds_bytes = 0;
+  const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  const size_t budget = dev.lds_per_block / sizeof(float);
+
+  // Whole rows, 8 output rows per tile if they fit; else fewer rows; else
+  // column tiles of a multiple of 4 output columns, 8 rows.
   a.TR = 0;
-  for (int tr = 8; tr >= 1; tr /= 2) {
-    const int plane = (tr + 2) * W;
-    const int cs = KS * plane + ((16 - (KS * plane) % 64) + 64) % 64;
-    const size_t bytes = (size_t)CI * cs * sizeof(float);
-    if (bytes <= dev.lds_per_block) {
+  a.TC = 0;
+  a.XC = 0;
+  size_t ring = 0;
+  for (int tr = 8; tr >= 2 && a.TR == 0; tr /= 2) {
+    const int xc = vl ? ((W + 3) & ~3) : W;
+    ring = ring_floats(tr, xc, &a.planestride, &a.chstride);
+    if (WS_FLOATS + ring + 2 * CO <= budget) {
       a.TR = tr;
-      a.planestride = plane;
-      a.chstride = cs;
-      lds_bytes = bytes;
-      break;
+      a.TC = a.Wo;
+      a.XC = xc;
     }
   }
-  if (a.TR == 0) return CCE_ERR_UNSUPPORTED;
+  if (a.TR == 0) {
+    a.TR = 8;
+    // Staged columns: TC + 2 rounded up to a multiple of 4.
+    for (int tc = (a.Wo - 1) & ~3; tc >= 4; tc -= 4) {
+      const int xc = (tc + 2 + 3) & ~3;
+      ring = ring_floats(a.TR, xc, &a.planestride, &a.chstride);
+      if (WS_FLOATS + ring + 2 * CO <= budget) {
+        a.TC = tc;
+        a.XC = xc;
+        break;
+      }
+    }
+    if (a.TC <= 0 || a.TC >= a.Wo) return CCE_ERR_UNSUPPORTED;
+  }
+  const size_t lds_bytes = (WS_FLOATS + ring + 2 * CO) * sizeof(float);
   a.rowtiles = (a.Ho + a.TR - 1) / a.TR;
-  const long long nt = (long long)N * a.Do * a.rowtiles;
-  if (nt >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
-  a.ntiles = (int)nt;
-  a.divDo = make_fastdiv((uint32_t)a.Do);
-  a.divRowtiles = make_fastdiv((uint32_t)a.rowtiles);
-  a.divWo = make_fastdiv((uint32_t)a.Wo);
+  a.coltiles = (a.Wo + a.TC - 1) / a.TC;
+  const long long nb = (long long)N * a.rowtiles * a.coltiles;
+  if (nb >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
+  a.nblocks = (int)nb;
+  a.divRowCol = make_fastdiv((uint32_t)(a.rowtiles * a.coltiles));
+  a.divCol = make_fastdiv((uint32_t)a.coltiles);
+  a.divTC = make_fastdiv((uint32_t)a.TC);
+  a.divTClast = make_fastdiv((uint32_t)(a.Wo - (a.coltiles - 1) * a.TC));
 
-  const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
-  const bool vs = ((a.Ho * a.Wo) % 4 == 0) && ((a.TR * a.Wo) % 4 == 0) && ((uintptr_t)y % 16 == 0);
+  // 16-byte stores need every lane's four voxels consecutive and aligned:
+  // whole-row tiles need (TR Wo) and (Ho Wo) multiples of 4; column tiles
+  // need Wo % 4 == 0 (TC is a multiple of 4).
+  const bool y16 = (uintptr_t)y % 16 == 0;
+  const bool vs = y16 && (a.coltiles == 1 ? ((a.Ho * a.Wo) % 4 == 0 && (a.TR * a.Wo) % 4 == 0)
+                                          : (a.Wo % 4 == 0));
   if (vl) return vs ? launch_series<true, true>(a, lds_bytes, dev, stream)
                     : launch_series<true, false>(a, lds_bytes, dev, stream);
   return vs ? launch_series<false, true>(a, lds_bytes, dev, stream)

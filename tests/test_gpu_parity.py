@@ -115,6 +115,8 @@ CONV3D_SMALL = [  # (N, D, H, W, bias)
     (2, 6, 21, 19, True),   # ragged row tiles, odd widths: scalar paths
     (3, 4, 22, 64, False),  # NULL bias, 4 row tiles of 8 (last one 4 rows)
     (1, 16, 64, 64, True),  # one image of the Conv3d workload
+    (1, 4, 20, 300, True),  # rows too wide for LDS: column tiles of 76, the last one ragged
+    (1, 3, 11, 512, False),  # widest supported rows
 ]
 
 
