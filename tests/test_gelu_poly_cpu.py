@@ -1,0 +1,42 @@
+"""The device-side GELU polynomial used on [-1, 1] (csrc/cce_device.hpp,
+gelu_small): its coefficients, read from the header, must reproduce
+GELU(t) = 0.5 t (1 + erf(t / sqrt 2)) within 2e-8 on [-1, 1] when evaluated
+in double, and within fp32 rounding (2e-7) when evaluated in fp32 the way the
+kernel does (Horner in u = t^2, then u * r + 0.5 t)."""
+import re
+from pathlib import Path
+
+import numpy as np
+from scipy.special import erf
+
+HDR = Path(__file__).resolve().parents[1] / "channel_convolution_epilogue_amd" / "csrc" / "cce_device.hpp"
+
+
+def coefficients():
+    src = HDR.read_text()
+    body = src[src.index("float gelu_small(float t)"):]
+    body = body[:body.index("}")]
+    first = re.search(r"float r = ([-+0-9.eE]+)f;", body).group(1)
+    rest = re.findall(r"r = fmaf\(r, u, ([-+0-9.eE]+)f\);", body)
+    return [float(first)] + [float(c) for c in rest]  # highest degree first
+
+
+def test_gelu_polynomial_error_bound():
+    c = coefficients()
+    assert len(c) == 5
+    t = np.linspace(-1.0, 1.0, 400001)
+    exact = 0.5 * t * (1.0 + erf(t / np.sqrt(2.0)))
+    u = t * t
+    r = np.zeros_like(t)
+    for ck in c:
+        r = r * u + ck
+    assert np.abs(0.5 * t + u * r - exact).max() < 2e-8
+
+    t32, u32 = t.astype(np.float32), (t.astype(np.float32) ** 2).astype(np.float32)
+    r32 = np.full_like(t32, np.float32(c[0]))
+    for ck in c[1:]:
+        r32 = (r32 * u32 + np.float32(ck)).astype(np.float32)
+    y32 = (u32 * r32 + np.float32(0.5) * t32).astype(np.float32)
+    assert np.abs(y32.astype(np.float64) - exact).max() < 2e-7
+    # the t -> 0 limit: slope 1/2 and curvature 1/sqrt(2 pi)
+    assert abs(c[-1] - 1.0 / np.sqrt(2.0 * np.pi)) < 1e-6

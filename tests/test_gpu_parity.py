@@ -264,6 +264,23 @@ def test_elementwise_tail_small(cce, N, C, D, H, W):
                      f"elementwise tail {N}x{C}x{D}x{H}x{W} clamp [{lo},{hi}]")
 
 
+@pytest.mark.parametrize("slope,lo,hi", [(0.2, -1.0, 1.0), (1.0, -1.0, 1.0), (1.5, -0.5, 0.25),
+                                          (-0.3, -1.0, 1.0), (0.2, -3.0, 4.0)])
+def test_epilogue_fp32_accuracy(cce, slope, lo, hi):
+    """The LeakyReLU/add/clamp/GELU chain on a dense sweep of inputs, held to
+    fp32 accuracy (2e-7 + 2e-7 |ref|: a few roundings of the fp32 chain)
+    rather than the operators' 1e-4: covers the polynomial GELU (clamp inside
+    [-1, 1]), erff (clamp outside), slopes above 1 and below 0 (the median
+    form of LeakyReLU)."""
+    z = np.linspace(-6.0, 6.0, 1 << 20).astype(np.float32).reshape(1, 4, -1)
+    s = np.array([0.0, 0.37, -0.81, 1.9], np.float32)
+    y = cce.lrelu_add_clamp_gelu(dev(z), dev(s), slope, lo, hi)
+    torch.cuda.synchronize()
+    ref = O.lrelu_add_clamp_gelu_array(z, s, slope, lo, hi)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ref) - 2e-7 * np.abs(ref)
+    assert err.max() < 2e-7, f"max excess error {err.max():.3e} (slope {slope}, clamp [{lo}, {hi}])"
+
+
 def test_elementwise_tail_workload_sampled(cce):
     shape, p = workload_inputs("lrelu_add_clamp_gelu_n128", seed=0)
     y = cce.lrelu_add_clamp_gelu(dev(p["z"]), dev(p["s"]), shape["slope"], shape["lo"], shape["hi"])
