@@ -214,7 +214,24 @@ def device_inputs(torch, cce, shape, p):
     return d
 
 
-def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0):
+def per_call_times(torch, fn, calls, evict=None):
+    """Median and minimum of `calls` individually event-timed calls on the
+    current stream.  With `evict`, it runs before every call (outside the
+    events) -- a 1 GiB scratch write that flushes the L2s and the 256 MB MALL."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for e0, e1 in evs:
+        if evict is not None:
+            evict()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return {"median_ms": round(ts[len(ts) // 2], 5), "min_ms": round(ts[0], 5), "calls": calls}
+
+
+def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0, cold_calls=0):
     shape, p = workload_inputs(name, seed)
     d = device_inputs(torch, cce, shape, p)
     del p
@@ -260,9 +277,52 @@ def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0):
                            "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
                            "traffic": measured_traffic(shape["op"], name)}
     out["hbm_frac"] = round(out["gbs"] / PEAK_HBM_GBS, 4)
+    # Per-call distributions: hot (back to back, as above) and cold.
+    out["hot"] = per_call_times(torch, fn, min(steps, 100))
+    if cold_calls:
+        scratch = torch.empty(1 << 28, device="cuda")  # 1 GiB
+        out["cold"] = per_call_times(torch, fn, cold_calls, evict=lambda: scratch.fill_(1.0))
+        del scratch
     del d
     torch.cuda.empty_cache()
     return shape, out
+
+
+def unfused_torch(torch, name, steps, seed):
+    """Context only: the same workload as PyTorch-ROCm's eager sequence of
+    separate operators (MIOpen convolution, then each elementwise / pooling /
+    reduction op as its own kernel, every intermediate in HBM), fp32."""
+    import torch.nn.functional as F
+    shape, p = workload_inputs(name, seed)
+    op = shape["op"]
+    if op not in (CONV2D, CONV3D, CONVT):
+        return None
+    d = {k: torch.from_numpy(v).cuda() for k, v in p.items()}
+    del p
+    if op == CONV2D:
+        fn = lambda: F.hardswish(F.relu(F.conv2d(d["x"], d["w"], d["b"])))  # noqa: E731
+    elif op == CONV3D:
+        s5 = d["s"].view(1, -1, 1, 1, 1)
+        fn = lambda: F.gelu(torch.clamp(F.leaky_relu(F.conv3d(d["x"], d["w"], d["b"]),  # noqa: E731
+                                                     shape["slope"]) + s5, shape["lo"], shape["hi"]))
+    else:
+        fn = lambda: torch.tanh(torch.mean(F.hardtanh(F.max_pool2d(  # noqa: E731
+            F.conv_transpose2d(d["x"], d["w"], d["b"], stride=1, padding=1), 2, 2),
+            shape["lo"], shape["hi"]), dim=(2, 3), keepdim=True))
+    for _ in range(3):  # first calls pick and compile the convolution kernels
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del d
+    torch.cuda.empty_cache()
+    return round(ms, 5)
 
 
 def cpu_baseline(name, seed, budget_s=12.0):
@@ -343,6 +403,10 @@ def main():
                     help="only convert rocprofv3 FETCH_SIZE/WRITE_SIZE runs in PMC_DIR into "
                          "profiles/hbm_traffic.json and exit")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy")
+    ap.add_argument("--unfused", action="store_true",
+                    help="also time PyTorch-ROCm's unfused operator sequence per workload (context)")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="calls timed one by one after a 1 GiB cache-flushing write (0: skip)")
     args = ap.parse_args()
 
     if args.record_traffic:
@@ -371,7 +435,7 @@ def main():
     cce.load()
 
     shape, head = time_workload(torch, cce, args.workload, args.steps, args.warmup, args.seed,
-                                args.prewarm)
+                                args.prewarm, args.cold_calls)
     print(f"# {args.workload}: {head['ms_per_call']:.4f} ms/call, {head['gflops']:.1f} GFLOP/s, "
           f"{head['gbs']:.1f} GB/s, {head['roofline']['frac']:.3f} of the {head['roofline']['bound']} roofline",
           file=sys.stderr, flush=True)
@@ -382,14 +446,16 @@ def main():
                 r = head
             else:
                 _, r = time_workload(torch, cce, name, max(3, min(args.steps, 50)), min(args.warmup, 10),
-                                     args.seed, min(args.prewarm, 0.5))
+                                     args.seed, min(args.prewarm, 0.5), min(args.cold_calls, 10))
                 print(f"# {name}: {r['ms_per_call']:.4f} ms/call, {r['gflops']:.1f} GFLOP/s, "
                       f"{r['gbs']:.1f} GB/s, {r['roofline']['frac']:.3f} of the "
                       f"{r['roofline']['bound']} roofline", file=sys.stderr, flush=True)
             ops[name] = {"ms_per_call": round(r["ms_per_call"], 5), "gflops": round(r["gflops"], 1),
                          "gbs": round(r["gbs"], 1), "roofline_bound": r["roofline"]["bound"],
                          "roofline_frac": r["roofline"]["frac"],
-                         "hbm_frac": r["hbm_frac"]}
+                         "hbm_frac": r["hbm_frac"], "hot": r["hot"]}
+            if "cold" in r:
+                ops[name]["cold"] = r["cold"]
 
     line = {
         "metric": METRIC,
@@ -410,7 +476,22 @@ def main():
         "roofline": head["roofline"],
         "hbm": {"achieved": round(head["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": head["hbm_frac"]},
+        # per-call event timing: hot = back to back; cold = after a 1 GiB write
+        # that flushes the L2s and the MALL (the event pair brackets the kernel only)
+        "per_call": {k: head[k] for k in ("hot", "cold") if k in head},
     }
+    if args.unfused:
+        names = list(WORKLOADS) if args.ops == "all" else [args.workload]
+        ctx = {}
+        for name in names:
+            ms = unfused_torch(torch, name, max(3, min(args.steps, 20)), args.seed)
+            if ms is None:
+                continue
+            fused = ops[name]["ms_per_call"] if name in ops else head["ms_per_call"]
+            ctx[name] = {"ms_per_call": ms, "fused_speedup": round(ms / fused, 2)}
+            print(f"# unfused torch {name}: {ms:.4f} ms/call ({ms / fused:.2f}x the fused kernel)",
+                  file=sys.stderr, flush=True)
+        line["unfused_torch"] = ctx
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.seed)
     if ops:
