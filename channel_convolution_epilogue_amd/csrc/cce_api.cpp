@@ -143,11 +143,11 @@ int pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, i
   if (!z || !y) return CCE_ERR_NULL;
   if (N < 1 || C < 1 || H < 1 || W < 1 || pool_k < 1 || pool_s < 1) return CCE_ERR_SHAPE;
   if (H < pool_k || W < pool_k) return CCE_ERR_SHAPE;
-  if (pool_k != 2 || pool_s != 2) return CCE_ERR_UNSUPPORTED;
   if (!is_finite_f(htanh_lo) || !is_finite_f(htanh_hi) || htanh_lo > htanh_hi) return CCE_ERR_UNSUPPORTED;
   if (!aligned4(z) || !aligned4(y)) return CCE_ERR_ALIGN;
   if ((long long)N * C >= (1LL << 31) || (long long)H * W >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
-  return cce::launch_pool_htanh_mean_tanh(z, y, N, C, H, W, htanh_lo, htanh_hi, (hipStream_t)stream);
+  return cce::launch_pool_htanh_mean_tanh(z, y, N, C, H, W, pool_k, pool_s, htanh_lo, htanh_hi,
+                                          (hipStream_t)stream);
 }
 
 int lrelu_add_clamp_gelu(const float *z, const float *s, float *y, int N, int C, long long S,

@@ -34,8 +34,8 @@ int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const fl
                                         hipStream_t stream);
 
 // Epilogue-only operators over a precomputed convolution output.
-int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, float lo,
-                                float hi, hipStream_t stream);
+int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, int pool_k,
+                                int pool_s, float lo, float hi, hipStream_t stream);
 int launch_lrelu_add_clamp_gelu(const float *z, const float *s, float *y, int N, int C, long long S,
                                 float slope, float lo, float hi, hipStream_t stream);
 

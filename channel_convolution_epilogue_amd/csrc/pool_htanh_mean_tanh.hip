@@ -1,5 +1,5 @@
 // Epilogue-only tail of the transposed-conv model over a precomputed conv
-// output z[N][C][H][W]: y[n, c] = tanh(mean(Hardtanh(MaxPool2d(z[n, c], 2, 2)))).
+// output z[N][C][H][W]: y[n, c] = tanh(mean(Hardtanh(MaxPool2d(z[n, c], k, s)))).
 // This is the path POPCORNBENCH Kimi-K2.6 l2_p10 implemented (a library
 // transposed convolution followed by one fused tail kernel); here it is the
 // HBM-read-bound companion of the fully fused operator.
@@ -9,7 +9,9 @@
 // loads give two 2x2 windows.  Consecutive threads read consecutive quads, so
 // a wave reads 1 KB of a row per load.  Loads are issued four pairs ahead.
 // Window sums are reduced in a fixed order (lane -> wave -> workgroup), so the
-// result is deterministic.
+// result is deterministic.  Other window sizes and strides (overlapping or
+// gapped windows, floor output size) take a general path: one window per
+// thread, its k x k maximum read directly.
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
 
@@ -22,19 +24,32 @@ struct TailArgs {
   const float *__restrict__ z;
   float *__restrict__ y;
   int H, W, PH, PW;
+  int pk, ps;  // window size and stride (general path)
   float lo, hi, inv_count;
 };
+
+enum TailPath { kVec2 = 0, kScalar2 = 1, kGeneral = 2 };
 
 __device__ __forceinline__ float window(float a, float b, float c, float d, float lo, float hi) {
   return clampf(fmaxf(fmaxf(a, b), fmaxf(c, d)), lo, hi);
 }
 
-template <bool VEC>
+template <int PATH>
 __global__ __launch_bounds__(THREADS) void pool_htanh_mean_tanh_kernel(TailArgs a) {
   __shared__ float red[WAVES];
   const float *plane = a.z + (size_t)blockIdx.x * a.H * a.W;
   float sum = 0.0f;
-  if (VEC) {
+  if (PATH == kGeneral) {
+    const int units = a.PH * a.PW;
+    for (int u = threadIdx.x; u < units; u += THREADS) {
+      const int ph = u / a.PW, pw = u - ph * a.PW;
+      const float *p = plane + (size_t)(ph * a.ps) * a.W + pw * a.ps;
+      float m = p[0];
+      for (int dh = 0; dh < a.pk; ++dh)
+        for (int dw = 0; dw < a.pk; ++dw) m = fmaxf(m, p[(size_t)dh * a.W + dw]);
+      sum += clampf(m, a.lo, a.hi);
+    }
+  } else if (PATH == kVec2) {
     // unit u = (ph, q): rows 2ph and 2ph + 1, columns 4q .. 4q + 3 (windows 2q, 2q + 1)
     const int QW = a.PW >> 1;  // W % 4 == 0, so PW is even and QW = W / 4
     const int units = a.PH * QW;
@@ -85,26 +100,32 @@ __global__ __launch_bounds__(THREADS) void pool_htanh_mean_tanh_kernel(TailArgs 
 
 }  // namespace
 
-int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, float lo,
-                                float hi, hipStream_t stream) {
+int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, int pool_k,
+                                int pool_s, float lo, float hi, hipStream_t stream) {
   TailArgs a;
   a.z = z;
   a.y = y;
   a.H = H;
   a.W = W;
-  a.PH = H / 2;
-  a.PW = W / 2;
+  a.pk = pool_k;
+  a.ps = pool_s;
+  a.PH = (H - pool_k) / pool_s + 1;  // floor, as MaxPool2d without padding
+  a.PW = (W - pool_k) / pool_s + 1;
   a.lo = lo;
   a.hi = hi;
   a.inv_count = (float)(1.0 / ((double)a.PH * (double)a.PW));
   const long long planes = (long long)N * C;
   if (planes >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
-  const bool vec = (W % 4 == 0) && ((uintptr_t)z % 16 == 0);
+  const bool two = pool_k == 2 && pool_s == 2;
+  const bool vec = two && (W % 4 == 0) && ((uintptr_t)z % 16 == 0);
   if (vec)
-    hipLaunchKernelGGL(pool_htanh_mean_tanh_kernel<true>, dim3((unsigned)planes), dim3(THREADS), 0,
+    hipLaunchKernelGGL(pool_htanh_mean_tanh_kernel<kVec2>, dim3((unsigned)planes), dim3(THREADS), 0,
+                       stream, a);
+  else if (two)
+    hipLaunchKernelGGL(pool_htanh_mean_tanh_kernel<kScalar2>, dim3((unsigned)planes), dim3(THREADS), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL(pool_htanh_mean_tanh_kernel<false>, dim3((unsigned)planes), dim3(THREADS), 0,
+    hipLaunchKernelGGL(pool_htanh_mean_tanh_kernel<kGeneral>, dim3((unsigned)planes), dim3(THREADS), 0,
                        stream, a);
   return launch_status();
 }

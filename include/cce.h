@@ -150,10 +150,12 @@ size_t convT2d_pool_htanh_mean_tanh_workspace_bytes(int N, int C_in, int H, int 
  *   z  [N][C][H][W]   e.g. the transposed-conv output
  *   y  [N][C]         (the [N,C,1,1] result)
  *
- * Pooled size floor((H - pool_k) / pool_s) + 1 per axis; the mean divides by
- * the pooled element count.  Deterministic (fixed summation order).
- * Supported: pool_k = pool_s = 2, H, W >= 2, htanh_lo <= htanh_hi (finite),
- * N*C < 2^31.
+ * Pooled size floor((H - pool_k) / pool_s) + 1 per axis (windows may overlap
+ * when pool_s < pool_k, or skip elements when pool_s > pool_k); the mean
+ * divides by the pooled element count.  Deterministic (fixed summation order).
+ * Supported: any pool_k, pool_s >= 1 with H, W >= pool_k (else
+ * CCE_ERR_SHAPE), htanh_lo <= htanh_hi (finite), N*C < 2^31 and H*W < 2^31.
+ * pool_k = pool_s = 2 takes the streaming fast path.
  */
 int pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, int pool_k,
                          int pool_s, float htanh_lo, float htanh_hi, void *stream);

@@ -136,7 +136,8 @@ def test_tail_validation(lib):
     assert pt(z=None) == ENULL
     assert pt(H=1) == ESHAPE
     assert pt(N=0) == ESHAPE
-    assert pt(pk=3, ps=3) == EUNSUP
+    assert pt(pk=9) == ESHAPE  # window larger than the plane
+    assert pt(ps=0) == ESHAPE
     assert pt(lo=1.0, hi=0.0) == EUNSUP
     assert pt(y=FAKE + 1) == EALIGN
     assert pt(N=1 << 20, C=1 << 12) == ETOOBIG

@@ -243,6 +243,19 @@ def test_pool_tail_small(cce, N, C, H, W):
     assert_close(y.cpu().numpy()[:, :, 0, 0], O.pool_htanh_mean_tanh(z), f"pool tail N={N} C={C} {H}x{W}")
 
 
+@pytest.mark.parametrize("pk,ps,H,W", [(3, 2, 37, 23), (2, 3, 20, 31), (1, 1, 9, 7), (3, 1, 12, 12),
+                                       (4, 4, 64, 64), (5, 3, 17, 40), (2, 2, 9, 14)])
+def test_pool_tail_general_window_and_stride(cce, pk, ps, H, W):
+    """General MaxPool2d(k, s): overlapping, gapped and degenerate windows (the
+    general path), and 2/2 on a width that is not a multiple of 4 (scalar path)."""
+    p = make_inputs(TAIL_POOL, seed=450 + 10 * pk + ps, N=2, C=5, H=H, W=W)
+    z = p["z"] * np.float32(0.7)
+    y = cce.pool_htanh_mean_tanh(dev(z), pk, ps)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy()[:, :, 0, 0], O.pool_htanh_mean_tanh(z, pk, ps),
+                 f"pool tail k={pk} s={ps} {H}x{W}")
+
+
 def test_pool_tail_workload_full(cce):
     shape, p = workload_inputs("pool_htanh_mean_tanh_n128", seed=0)
     y = cce.pool_htanh_mean_tanh(dev(p["z"]))

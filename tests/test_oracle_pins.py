@@ -445,6 +445,25 @@ def test_pool_tail_matches_torch_and_plane_function(shape):
     np.testing.assert_allclose(O.pool_htanh_mean_tanh(z, lo=-0.3, hi=0.7), ref2, rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("pk,ps", [(3, 2), (2, 3), (1, 1), (3, 1), (4, 4), (5, 3)])
+def test_pool_tail_general_window_and_stride(pk, ps):
+    """Overlapping (s < k), gapped (s > k) and degenerate windows against torch
+    float64 MaxPool2d (floor output size), plus closed forms: k = s = 1 is the
+    plain mean of the clamped plane, a window covering the plane is its max."""
+    rng = np.random.default_rng(30 + 7 * pk + ps)
+    z = (rng.standard_normal((2, 3, 13, 11)) * 1.5).astype(np.float32)
+    ref = torch.tanh(F.hardtanh(F.max_pool2d(_t64(z), pk, ps), -1, 1).mean(dim=(2, 3))).numpy()
+    np.testing.assert_allclose(O.pool_htanh_mean_tanh(z, pk, ps), ref, rtol=0, atol=1e-14)
+    if pk == 1 and ps == 1:
+        np.testing.assert_allclose(O.pool_htanh_mean_tanh(z, 1, 1),
+                                   np.tanh(np.clip(z.astype(np.float64), -1, 1).mean(axis=(2, 3))),
+                                   rtol=0, atol=1e-14)
+    sq = z[:, :, :11, :11]
+    np.testing.assert_allclose(O.pool_htanh_mean_tanh(np.ascontiguousarray(sq), 11, ps),
+                               np.tanh(np.clip(sq.astype(np.float64).max(axis=(2, 3)), -1, 1)),
+                               rtol=0, atol=1e-15)
+
+
 def test_pool_tail_of_convT_equals_fused_model():
     # The tail over the oracle's own transposed-conv output reproduces the fused model.
     p = make_inputs(CONVT, seed=21, N=2, C_in=64, H=6, W=10, C_out=64, k=3)
