@@ -214,6 +214,18 @@ def device_inputs(torch, cce, shape, p):
     return d
 
 
+# The pages' own back-of-envelope time estimates for the same workloads on
+# other GPUs (none of them measured): context only, never a target.
+PAGES_ESTIMATE = {
+    "conv2d_relu_hswish_n128": {"ms": [0.2, 0.3], "hardware": "H100 (assumed by the page)",
+                                "what": "fused Conv2d+ReLU+HardSwish, total estimate"},
+    "conv3d_lrelu_add_clamp_gelu_n128": {"ms": [7.5, 13.5], "hardware": "A100 (assumed by the page)",
+                                         "what": "fused Conv3d kernel, scenarios"},
+    "convT2d_pool_htanh_mean_tanh_n128": {"ms": [1.2, 1.5], "hardware": "H100 (assumed by the page)",
+                                          "what": "library ConvTranspose2d + fused tail"},
+}
+
+
 def per_call_times(torch, fn, calls, evict=None):
     """Median and minimum of `calls` individually event-timed calls on the
     current stream.  With `evict`, it runs before every call (outside the
@@ -231,7 +243,7 @@ def per_call_times(torch, fn, calls, evict=None):
     return {"median_ms": round(ts[len(ts) // 2], 5), "min_ms": round(ts[0], 5), "calls": calls}
 
 
-def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0, cold_calls=0):
+def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0, cold_calls=0, keep_output=False):
     shape, p = workload_inputs(name, seed)
     d = device_inputs(torch, cce, shape, p)
     del p
@@ -283,6 +295,10 @@ def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0, cold_cal
         scratch = torch.empty(1 << 28, device="cuda")  # 1 GiB
         out["cold"] = per_call_times(torch, fn, cold_calls, evict=lambda: scratch.fill_(1.0))
         del scratch
+    if keep_output:  # host copy of the last call's result, for the error check
+        fn()
+        torch.cuda.synchronize()
+        out["y"] = d["y"].cpu().numpy()
     del d
     torch.cuda.empty_cache()
     return shape, out
@@ -325,9 +341,24 @@ def unfused_torch(torch, name, steps, seed):
     return round(ms, 5)
 
 
-def cpu_baseline(name, seed, budget_s=12.0):
+def error_vs_oracle(gpu, ref):
+    """Max abs and rel error of the GPU result against the oracle over the
+    sampled outputs, and how many exceed the 1e-4 + 1e-4 |ref| tolerance."""
+    g = np.asarray(gpu, np.float64).reshape(-1)
+    r = np.asarray(ref, np.float64).reshape(-1)
+    err = np.abs(g - r)
+    rel = err / np.maximum(np.abs(r), 1e-30)
+    return {"outputs": int(r.size), "max_abs": float(err.max()), "max_rel_where_abs_ref_ge_1e-3":
+            float(rel[np.abs(r) >= 1e-3].max()) if np.any(np.abs(r) >= 1e-3) else 0.0,
+            "over_tolerance": int(np.count_nonzero(err > 1e-4 + 1e-4 * np.abs(r))),
+            "finite": bool(np.all(np.isfinite(g)))}
+
+
+def cpu_baseline(name, seed, budget_s=12.0, gpu_y=None):
     """The CPU oracle (double precision, OpenMP over all host cores) timed on a
-    bounded sample of the workload, scaled to GFLOP/s of the same algorithmic count."""
+    bounded sample of the workload, scaled to GFLOP/s of the same algorithmic
+    count.  With the GPU's result `gpu_y`, the same sample also gives the GPU's
+    error against the oracle."""
     import oracle as O
     shape, p = workload_inputs(name, seed)
     op = shape["op"]
@@ -345,10 +376,14 @@ def cpu_baseline(name, seed, budget_s=12.0):
         n = int(max(1, min(shape["N"], budget_s / max(one, 1e-6))))
         zs = np.ascontiguousarray(p["z"][:n])
         t = time.perf_counter()
-        run(zs)
+        ref = run(zs)
         dt = time.perf_counter() - t
-        return {"value": round(per_image * n / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
-                "kind": "oracle", "sample": f"{n} of {shape['N']} images", "seconds": round(dt, 3)}
+        res = {"value": round(per_image * n / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
+               "kind": "oracle", "sample": f"{n} of {shape['N']} images", "seconds": round(dt, 3)}
+        if gpu_y is not None:
+            g = gpu_y[:n, :, 0, 0] if op == TAIL_POOL else gpu_y[:n]
+            res["gpu_error"] = error_vs_oracle(g, ref)
+        return res
     if op in (CONV2D, CONV3D):
         # whole images, as many as fit the time budget (at least one)
         per_image = work_counts(dict(shape, N=1))["fma"]
@@ -363,12 +398,14 @@ def cpu_baseline(name, seed, budget_s=12.0):
         xs = np.ascontiguousarray(p["x"][:n])
         t = time.perf_counter()
         if op == CONV2D:
-            O.conv2d_relu_hswish(xs, p["w"], p["b"])
+            ref = O.conv2d_relu_hswish(xs, p["w"], p["b"])
         else:
-            O.conv3d_lrelu_add_clamp_gelu(xs, p["w"], p["b"], p["s"], shape["slope"], shape["lo"], shape["hi"])
+            ref = O.conv3d_lrelu_add_clamp_gelu(xs, p["w"], p["b"], p["s"], shape["slope"], shape["lo"],
+                                                shape["hi"])
         dt = time.perf_counter() - t
         sample = f"{n} of {shape['N']} images, full output"
         fma = per_image * n
+        gpu_part = None if gpu_y is None else gpu_y[:n]
     else:
         per_plane = work_counts(shape)["fma"] // (shape["N"] * shape["C_out"])
         t = time.perf_counter()
@@ -377,12 +414,16 @@ def cpu_baseline(name, seed, budget_s=12.0):
         count = int(max(cores, min(shape["N"] * shape["C_out"], budget_s / max(one, 1e-6))))
         idx = rng.choice(shape["N"] * shape["C_out"], size=count, replace=False)
         t = time.perf_counter()
-        O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], idx)
+        ref = O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], idx)
         dt = time.perf_counter() - t
         sample = f"{count} of {shape['N'] * shape['C_out']} (image, channel) outputs"
         fma = per_plane * count
-    return {"value": round(2 * fma / dt / 1e9, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 3)}
+        gpu_part = None if gpu_y is None else gpu_y.reshape(-1)[idx]
+    res = {"value": round(2 * fma / dt / 1e9, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": sample, "seconds": round(dt, 3)}
+    if gpu_part is not None:
+        res["gpu_error"] = error_vs_oracle(gpu_part, ref)
+    return res
 
 
 def main():
@@ -435,7 +476,8 @@ def main():
     cce.load()
 
     shape, head = time_workload(torch, cce, args.workload, args.steps, args.warmup, args.seed,
-                                args.prewarm, args.cold_calls)
+                                args.prewarm, args.cold_calls, keep_output=not args.no_cpu_baseline)
+    gpu_y = head.pop("y", None)
     print(f"# {args.workload}: {head['ms_per_call']:.4f} ms/call, {head['gflops']:.1f} GFLOP/s, "
           f"{head['gbs']:.1f} GB/s, {head['roofline']['frac']:.3f} of the {head['roofline']['bound']} roofline",
           file=sys.stderr, flush=True)
@@ -456,6 +498,8 @@ def main():
                          "hbm_frac": r["hbm_frac"], "hot": r["hot"]}
             if "cold" in r:
                 ops[name]["cold"] = r["cold"]
+            if name in PAGES_ESTIMATE:
+                ops[name]["pages_estimate"] = PAGES_ESTIMATE[name]
 
     line = {
         "metric": METRIC,
@@ -480,6 +524,8 @@ def main():
         # that flushes the L2s and the MALL (the event pair brackets the kernel only)
         "per_call": {k: head[k] for k in ("hot", "cold") if k in head},
     }
+    if args.workload in PAGES_ESTIMATE:
+        line["pages_estimate"] = PAGES_ESTIMATE[args.workload]
     if args.unfused:
         names = list(WORKLOADS) if args.ops == "all" else [args.workload]
         ctx = {}
@@ -493,7 +539,8 @@ def main():
                   file=sys.stderr, flush=True)
         line["unfused_torch"] = ctx
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload, args.seed)
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.seed, gpu_y=gpu_y)
+        line["gpu_error_vs_oracle"] = line["cpu_baseline"].pop("gpu_error", None)
     if ops:
         line["ops"] = ops
     print(json.dumps(line), flush=True)
