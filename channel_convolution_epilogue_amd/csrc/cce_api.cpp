@@ -70,17 +70,26 @@ const char *cce_status_string(int status) {
 
 int cce_version(void) { return 100; }
 
+// Layer shapes the Conv2d kernel is instantiated for (see the header).
+static bool conv2d_layer_supported(int C_in, int C_out, int k) {
+  const bool ci = C_in == 4 || C_in == 8 || C_in == 16;
+  const bool co = C_out == 16 || C_out == 32 || C_out == 64;
+  const bool ks = k == 1 || k == 3 || (k == 5 && C_in <= 8);
+  return ci && co && ks;
+}
+
 int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N, int C_in,
                        int H, int W, int C_out, int k, void *stream) {
   if (!x || !w || !y) return CCE_ERR_NULL;
   if (N < 1 || C_in < 1 || C_out < 1 || k < 1 || H < k || W < k) return CCE_ERR_SHAPE;
-  if (C_in != 8 || C_out != 64 || k != 3) return CCE_ERR_UNSUPPORTED;
+  if (!conv2d_layer_supported(C_in, C_out, k)) return CCE_ERR_UNSUPPORTED;
   if (!aligned4(x) || !aligned4(w) || !aligned4(y) || (b && !aligned4(b))) return CCE_ERR_ALIGN;
-  const long long P = (long long)(H - 2) * (W - 2);
+  const long long P = (long long)(H - k + 1) * (W - k + 1);
   if ((long long)N * P >= (1LL << 31) || (long long)N * H >= (1LL << 31) ||
-      (long long)C_in * H * W >= (1LL << 31) || (long long)N * C_in * H * W >= (1LL << 40))
+      (long long)C_in * H * W >= (1LL << 31) || (long long)C_out * P >= (1LL << 31) ||
+      (long long)N * C_in * H * W >= (1LL << 40))
     return CCE_ERR_TOO_LARGE;
-  return cce::launch_conv2d_relu_hswish(x, w, b, y, N, H, W, (hipStream_t)stream);
+  return cce::launch_conv2d_relu_hswish(x, w, b, y, N, C_in, H, W, C_out, k, (hipStream_t)stream);
 }
 
 int conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b, const float *s,

@@ -20,7 +20,7 @@ int current_device_info(DeviceInfo *info);  // CCE_OK or CCE_ERR_LAUNCH
 
 // Conv2d 3x3 (8 -> 64) + ReLU + HardSwish.  Arguments already validated.
 int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
-                              int H, int W, hipStream_t stream);
+                              int C_in, int H, int W, int C_out, int k, hipStream_t stream);
 
 // Conv3d 3x3x3 (8 -> 64) + LeakyReLU + add + clamp + GELU.  Validated.
 int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,

@@ -38,32 +38,35 @@
 namespace cce {
 namespace {
 
-constexpr int CI = 8, CO = 64, KS = 3, TAPS = KS * KS;
-constexpr int KSTEPS = (CI / 4) * TAPS;      // 18 steps of 4 taps
-constexpr int NT = CO / 16;                  // 4 channel blocks of 16
 constexpr int WAVES = 16, THREADS = 64 * WAVES;  // one workgroup per CU, 4 waves per SIMD
-constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // weights in LDS, B-operand order (18 KB)
 
-// Geometry of one wave's strip: RB output rows by CB blocks of 16 columns.
-// The staged window spans columns [c0 - 4, c0 + 16 CB + 4) (quad-aligned, and
-// wide enough for the 0..3 column shift and the 2-column halo) and RB + 2 rows.
-// Its channel planes are CS floats apart, CS = 16 or 48 mod 64, so the four
-// lane groups of an A read (four channels) start on four different quarters
-// of the 64 LDS banks.
+// Geometry of one wave's strip and of the layer: RB output rows by CB blocks
+// of 16 columns, for CI input channels (a multiple of 4: one per lane group
+// per K-step), CO output channels (16 per MFMA block, at most 64) and k x k
+// kernels.  The staged window spans columns [c0 - 4, c0 + 16 CB + 4 +
+// pad(k - 1)) (quad-aligned, wide enough for the 0..3 column shift and the
+// k - 1 halo) and RB + k - 1 rows.  Its channel planes are CS floats apart,
+// CS = 16 or 48 mod 64, so the four lane groups of an A read (four channels)
+// start on four different quarters of the 64 LDS banks.
 constexpr int chan_stride(int need) {
   int c = need;
   while (c % 64 != 16 && c % 64 != 48) ++c;
   return c;
 }
-template <int RB_, int CB_>
+template <int RB_, int CB_, int CI_, int CO_, int KS_>
 struct StripGeo {
   static constexpr int RB = RB_, CB = CB_, MT = RB * CB;
-  static constexpr int SW = 16 * CB;         // output columns per strip
-  static constexpr int XW = SW + 8;          // staged columns per row
-  static constexpr int XQ = XW / 4;          // 16-byte quads per staged row
-  static constexpr int ROWS = RB + KS - 1;   // staged rows
+  static constexpr int CI = CI_, CO = CO_, KS = KS_, TAPS = KS * KS;
+  static constexpr int KSTEPS = (CI / 4) * TAPS;  // K-steps of 4 taps
+  static constexpr int NT = CO / 16;              // 16-channel MFMA blocks
+  static constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // weights in LDS, B-operand order
+  static constexpr int SW = 16 * CB;              // output columns per strip
+  static constexpr int XW = SW + 4 + ((KS - 1 + 3) & ~3);  // staged columns per row
+  static constexpr int XQ = XW / 4;               // 16-byte quads per staged row
+  static constexpr int ROWS = RB + KS - 1;        // staged rows
   static constexpr int CS = chan_stride(ROWS * XW);
-  static constexpr int WIN = CI * CS;        // floats per wave window
+  static constexpr int WIN = CI * CS;             // floats per wave window
+  static_assert(CI % 4 == 0 && CO % 16 == 0 && NT >= 1 && NT <= 4 && KS % 2 == 1, "layer shape");
 };
 
 struct Conv2dArgs {
@@ -93,12 +96,30 @@ struct Strip {
   int n, r0, c0;
 };
 
+// A lane's B operands of one K-step for all NT channel blocks: one 16-, 8- or
+// 4-byte LDS read.
+template <int NT>
+__device__ __forceinline__ void load_b(float (&bv)[NT], const float *p) {
+  if constexpr (NT == 4) {
+    const v4f v = *reinterpret_cast<const v4f *>(p);
+    bv[0] = v.x, bv[1] = v.y, bv[2] = v.z, bv[3] = v.w;
+  } else if constexpr (NT == 2) {
+    const float2 v = *reinterpret_cast<const float2 *>(p);
+    bv[0] = v.x, bv[1] = v.y;
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bv[nt] = p[nt];
+  }
+}
+
 // VLOAD: W % 4 == 0 and x 16-byte aligned (16-byte window loads).
 // VSTORE: P % 4 == 0 and y 16-byte aligned (16-byte result stores).
 template <class GEO, bool VLOAD, bool VSTORE>
 __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dArgs a) {
   constexpr int RB = GEO::RB, CB = GEO::CB, MT = GEO::MT, SW = GEO::SW, XW = GEO::XW,
                 XQ = GEO::XQ, ROWS = GEO::ROWS, CS = GEO::CS, WIN = GEO::WIN;
+  constexpr int CI = GEO::CI, CO = GEO::CO, KS = GEO::KS, TAPS = GEO::TAPS, KSTEPS = GEO::KSTEPS,
+                NT = GEO::NT, WS_FLOATS = GEO::WS_FLOATS;
   extern __shared__ __attribute__((aligned(16))) float lds[];
   float *ws = lds;                                  // weights, WS_FLOATS
   float *win = lds + WS_FLOATS + (threadIdx.x >> 6) * WIN;  // this wave's window
@@ -108,7 +129,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   // B operand of K-step s = (half, kh, kw) for all four 16-channel blocks:
   // ws[s][lane][nt] = w[16 nt + lane % 16][4 half + lane / 16][kh][kw].
   for (int e = tid; e < WS_FLOATS; e += THREADS) {
-    const int nt = e & 3, ln = (e >> 2) & 63, st = e >> 8;
+    const int nt = e % NT, ln = (e / NT) & 63, st = e / (NT * 64);
     const int o = 16 * nt + (ln & 15), ci = 4 * (st / TAPS) + (ln >> 4);
     ws[e] = a.w[(o * CI + ci) * TAPS + (st % TAPS)];
   }
@@ -217,17 +238,15 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
     for (int s = 0; s < KSTEPS; ++s) {
       const int tap = s % TAPS;
       const int off = (s / TAPS) * 4 * CS + (tap / KS) * XW + (tap % KS);
-      const v4f bv = *reinterpret_cast<const v4f *>(&ws[(s * 64 + lane) * NT]);
+      float bv[NT];
+      load_b<NT>(bv, &ws[(s * 64 + lane) * NT]);
       float av[MT];
 #pragma unroll
       for (int j = 0; j < MT; ++j) av[j] = win[base[j] + off];
 #pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        acc[j][0] = mfma16x16x4(av[j], bv.x, acc[j][0]);
-        acc[j][1] = mfma16x16x4(av[j], bv.y, acc[j][1]);
-        acc[j][2] = mfma16x16x4(av[j], bv.z, acc[j][2]);
-        acc[j][3] = mfma16x16x4(av[j], bv.w, acc[j][3]);
-      }
+      for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[j][nt] = mfma16x16x4(av[j], bv[nt], acc[j][nt]);
     }
 
     // The window has been read (the MFMAs above consumed every value), so the
@@ -279,7 +298,7 @@ template <class GEO, bool VL, bool VS>
 int launch_instance(const Conv2dArgs &a, hipStream_t stream) {
   DeviceInfo dev;
   if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
-  const size_t lds_bytes = ((size_t)WS_FLOATS + (size_t)WAVES * GEO::WIN) * sizeof(float);
+  const size_t lds_bytes = ((size_t)GEO::WS_FLOATS + (size_t)WAVES * GEO::WIN) * sizeof(float);
   if (lds_bytes > dev.lds_per_block) return CCE_ERR_UNSUPPORTED;
   auto kern = conv2d_relu_hswish_kernel<GEO, VL, VS>;
   if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -297,14 +316,12 @@ int launch_instance(const Conv2dArgs &a, hipStream_t stream) {
   return launch_status();
 }
 
-}  // namespace
-
-int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
-                              int H, int W, hipStream_t stream) {
-  // Strips of 2 rows x 16 columns.  Measured on MI355X at N = 128 (ms):
-  // 2 x 16: 0.199, 1 x 16: 0.204, 1 x 32: 0.211, 3 x 16: 0.294 (spills);
-  // 16-wave workgroups 0.195 against 0.199 for 8-wave ones.
-  using Geo = StripGeo<2, 1>;
+// Strip decomposition of one layer shape and its launch.  ALL_PATHS: the
+// shape has instances with 16-byte loads and stores; otherwise only the
+// scalar-load, scalar-store instance exists.
+template <class GEO, bool ALL_PATHS>
+int launch_layer(const float *x, const float *w, const float *b, float *y, int N, int H, int W,
+                 hipStream_t stream) {
   Conv2dArgs a;
   a.x = x;
   a.w = w;
@@ -312,12 +329,12 @@ int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, fl
   a.y = y;
   a.H = H;
   a.W = W;
-  a.Ho = H - (KS - 1);
-  a.Wo = W - (KS - 1);
+  a.Ho = H - (GEO::KS - 1);
+  a.Wo = W - (GEO::KS - 1);
   a.P = a.Ho * a.Wo;
 
-  const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
-  const bool vs = (a.P % 4 == 0) && ((uintptr_t)y % 16 == 0);
+  const bool vl = ALL_PATHS && (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  const bool vs = ALL_PATHS && (a.P % 4 == 0) && ((uintptr_t)y % 16 == 0);
   // Largest left shift any row's strips take (0 when stores are scalar).
   int sh_max = 0;
   if (vs)
@@ -325,16 +342,47 @@ int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, fl
       const int sh = (r * (a.Wo & 3)) & 3;
       if (sh > sh_max) sh_max = sh;
     }
-  a.S = (a.Wo + sh_max + Geo::SW - 1) / Geo::SW;
-  a.G = (a.Ho + Geo::RB - 1) / Geo::RB;
+  a.S = (a.Wo + sh_max + GEO::SW - 1) / GEO::SW;
+  a.G = (a.Ho + GEO::RB - 1) / GEO::RB;
   const long long items = (long long)N * a.G * a.S;
   if (items >= (1LL << 31) - (1LL << 24)) return CCE_ERR_TOO_LARGE;
   a.items = (int)items;
   a.divS = make_fastdiv((uint32_t)a.S);
   a.divG = make_fastdiv((uint32_t)a.G);
 
-  if (vl) return vs ? launch_instance<Geo, true, true>(a, stream) : launch_instance<Geo, true, false>(a, stream);
-  return vs ? launch_instance<Geo, false, true>(a, stream) : launch_instance<Geo, false, false>(a, stream);
+  if constexpr (ALL_PATHS) {
+    if (vl) return vs ? launch_instance<GEO, true, true>(a, stream) : launch_instance<GEO, true, false>(a, stream);
+    return vs ? launch_instance<GEO, false, true>(a, stream) : launch_instance<GEO, false, false>(a, stream);
+  } else {
+    return launch_instance<GEO, false, false>(a, stream);
+  }
+}
+
+}  // namespace
+
+int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
+                              int C_in, int H, int W, int C_out, int k, hipStream_t stream) {
+  // The page's layer, 8 -> 64 channels, 3 x 3: strips of 2 rows x 16 columns
+  // and every 16-byte path.  Measured on MI355X at N = 128 (ms): 2 x 16:
+  // 0.199, 1 x 16: 0.204, 1 x 32: 0.211, 3 x 16: 0.294 (spills); 16-wave
+  // workgroups 0.195 against 0.199 for 8-wave ones.
+  if (C_in == 8 && C_out == 64 && k == 3)
+    return launch_layer<StripGeo<2, 1, 8, 64, 3>, true>(x, w, b, y, N, H, W, stream);
+  // Other layer shapes whose weights and 16 wave windows fit in LDS: C_in of
+  // 4, 8 or 16, C_out of 16, 32 or 64, 1 x 1, 3 x 3 or 5 x 5 kernels (5 x 5
+  // up to 8 input channels); scalar loads and stores.
+#define CCE_CONV2D_LAYER(CI, CO, KS)                                                        \
+  if (C_in == CI && C_out == CO && k == KS)                                                \
+    return launch_layer<StripGeo<2, 1, CI, CO, KS>, false>(x, w, b, y, N, H, W, stream);
+#define CCE_CONV2D_LAYERS_CO(CI, KS) \
+  CCE_CONV2D_LAYER(CI, 16, KS) CCE_CONV2D_LAYER(CI, 32, KS) CCE_CONV2D_LAYER(CI, 64, KS)
+  CCE_CONV2D_LAYERS_CO(4, 1) CCE_CONV2D_LAYERS_CO(8, 1) CCE_CONV2D_LAYERS_CO(16, 1)
+  CCE_CONV2D_LAYERS_CO(4, 3) CCE_CONV2D_LAYER(8, 16, 3) CCE_CONV2D_LAYER(8, 32, 3)
+  CCE_CONV2D_LAYERS_CO(16, 3)
+  CCE_CONV2D_LAYERS_CO(4, 5) CCE_CONV2D_LAYERS_CO(8, 5)
+#undef CCE_CONV2D_LAYERS_CO
+#undef CCE_CONV2D_LAYER
+  return CCE_ERR_UNSUPPORTED;
 }
 
 }  // namespace cce

@@ -70,10 +70,13 @@ int cce_version(void);
  * padding 0, the defaults the page's problem uses), r = max(z, 0),
  * y = r * clamp((r + 3) / 6, 0, 1).
  *
- * Supported: C_in = 8, C_out = 64, k = 3, any N >= 1, H, W >= 3; other
- * channel counts or kernel sizes return CCE_ERR_UNSUPPORTED.  One input image
- * (8*H*W floats) and the output pixel count N*(H-2)*(W-2) must stay below
- * 2^31, else CCE_ERR_TOO_LARGE.
+ * Supported layers: the page's C_in = 8, C_out = 64, k = 3 (the tuned
+ * instance, 16-byte loads and stores), and C_in in {4, 8, 16}, C_out in
+ * {16, 32, 64}, k in {1, 3, 5} (k = 5 only for C_in <= 8; scalar loads and
+ * stores); any N >= 1 and H, W >= k.  Other layers return
+ * CCE_ERR_UNSUPPORTED.  One input image (C_in*H*W floats), one output image
+ * and the output pixel count N*(H-k+1)*(W-k+1) must stay below 2^31, else
+ * CCE_ERR_TOO_LARGE.
  */
 int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N, int C_in,
                        int H, int W, int C_out, int k, void *stream);

@@ -61,8 +61,10 @@ def test_conv2d_validation(lib):
     assert c2(lib, H=2) == ESHAPE
     assert c2(lib, W=-5) == ESHAPE
     assert c2(lib, C_in=3) == EUNSUP
-    assert c2(lib, C_out=32) == EUNSUP
-    assert c2(lib, k=5) == EUNSUP
+    assert c2(lib, C_in=32) == EUNSUP
+    assert c2(lib, C_out=48) == EUNSUP
+    assert c2(lib, k=2) == EUNSUP
+    assert c2(lib, C_in=16, k=5) == EUNSUP  # weights and windows exceed LDS
     assert c2(lib, H=1 << 15, W=1 << 13) == ETOOBIG  # one image of 2^31 floats
     assert c2(lib, x=FAKE + 2) == EALIGN
     assert c2(lib, b=FAKE + 1) == EALIGN

@@ -82,6 +82,19 @@ def test_conv2d_small(cce, N, H, W, bias):
     assert_close(y.cpu().numpy(), O.conv2d_relu_hswish(p["x"], p["w"], b), f"conv2d N={N} {H}x{W}")
 
 
+@pytest.mark.parametrize("C_in,C_out,k", [(4, 16, 1), (8, 32, 3), (16, 64, 3), (4, 64, 5), (8, 16, 5),
+                                         (16, 32, 1), (8, 64, 1), (4, 32, 3)])
+def test_conv2d_other_layer_shapes(cce, C_in, C_out, k):
+    """Layer shapes beyond the page's 8 -> 64, 3 x 3 (other channel counts and
+    kernel sizes), on odd sizes that leave ragged strips and row groups."""
+    p = make_inputs(CONV2D, seed=600 + C_in + C_out + k, N=2, C_in=C_in, H=19, W=23, C_out=C_out, k=k)
+    y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
+    torch.cuda.synchronize()
+    assert y.shape == (2, C_out, 19 - k + 1, 23 - k + 1)
+    assert_close(y.cpu().numpy(), O.conv2d_relu_hswish(p["x"], p["w"], p["b"]),
+                 f"conv2d {C_in}->{C_out} k={k}")
+
+
 def test_conv2d_workload_n8_full(cce):
     shape, p = workload_inputs("conv2d_relu_hswish_n8", seed=0)
     y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
