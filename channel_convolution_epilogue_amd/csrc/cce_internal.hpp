@@ -24,8 +24,9 @@ int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, fl
 
 // Conv3d 3x3x3 (8 -> 64) + LeakyReLU + add + clamp + GELU.  Validated.
 int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,
-                                       const float *s, float *y, int N, int D, int H, int W,
-                                       float slope, float lo, float hi, hipStream_t stream);
+                                       const float *s, float *y, int N, int C_in, int D, int H,
+                                       int W, int C_out, float slope, float lo, float hi,
+                                       hipStream_t stream);
 
 // ConvTranspose2d 3x3 s1 p1 (64 -> 64) + MaxPool 2x2 + Hardtanh + mean + tanh.
 size_t convT_workspace_bytes(int N, int H, int W);

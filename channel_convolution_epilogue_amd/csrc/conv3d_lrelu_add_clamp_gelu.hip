@@ -30,11 +30,19 @@
 namespace cce {
 namespace {
 
-constexpr int CI = 8, CO = 64, KS = 3, TAPS = KS * KS * KS;
-constexpr int KSTEPS = (CI / 4) * TAPS;      // 54 steps of 4 taps
-constexpr int NT = CO / 16;                  // 4 channel blocks of 16
+constexpr int KS = 3, TAPS = KS * KS * KS;
 constexpr int WAVES = 16, THREADS = 64 * WAVES;  // one workgroup per CU, 4 waves per SIMD
-constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // 13824 floats (55 KB)
+
+// Layer shape: CI input channels (a multiple of 4: one per lane group per
+// K-step), CO output channels (16 per MFMA block, at most 64).
+template <int CI_, int CO_>
+struct Layer3 {
+  static constexpr int CI = CI_, CO = CO_;
+  static constexpr int KSTEPS = (CI / 4) * TAPS;      // K-steps of 4 taps (54 for 8 channels)
+  static constexpr int NT = CO / 16;                  // 16-channel MFMA blocks
+  static constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // weights, B-operand order (55 KB for 8 -> 64)
+  static_assert(CI % 4 == 0 && CO % 16 == 0 && NT >= 1 && NT <= 4, "layer shape");
+};
 constexpr int SLOTS = 4;                     // input planes held in LDS
 constexpr int MT = 2;                        // 16-voxel blocks per wave per pass
 constexpr int kPrefetchPasses = 2;           // a plane of 8 x 10 rows of 64 floats takes 2 passes
@@ -59,22 +67,40 @@ struct Conv3dArgs {
 };
 
 // One staged input plane dd of a row-column block: staged row `row` =
-// rr * 8 + ci <-> x[n][ci][dd][h0 + rr][c0 ...], stored in ring slot dd % 4.
+// rr * CI + ci <-> x[n][ci][dd][h0 + rr][c0 ...], stored in ring slot dd % 4.
+template <int CI>
 struct PlaneSrc {
   const float *x;
   int D, H, W, n, dd, h0, c0;
   __device__ __forceinline__ const float *operator()(int row) const {
-    const int ci = row & (CI - 1), rr = row >> 3;
+    const int ci = row % CI, rr = row / CI;
     return x + ((((size_t)n * CI + ci) * D + dd) * H + (h0 + rr)) * W + c0;
   }
 };
+template <int CI>
 struct PlaneDst {
   float *xs;
   int chstride, slot_off, XC;
   __device__ __forceinline__ float *operator()(int row) const {
-    return xs + (row & (CI - 1)) * chstride + slot_off + (row >> 3) * XC;
+    return xs + (row % CI) * chstride + slot_off + (row / CI) * XC;
   }
 };
+
+// A lane's B operands of one K-step for all NT channel blocks: one 16-, 8- or
+// 4-byte LDS read.
+template <int NT>
+__device__ __forceinline__ void load_b(float (&bv)[NT], const float *p) {
+  if constexpr (NT == 4) {
+    const v4f v = *reinterpret_cast<const v4f *>(p);
+    bv[0] = v.x, bv[1] = v.y, bv[2] = v.z, bv[3] = v.w;
+  } else if constexpr (NT == 2) {
+    const float2 v = *reinterpret_cast<const float2 *>(p);
+    bv[0] = v.x, bv[1] = v.y;
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bv[nt] = p[nt];
+  }
+}
 
 // LDS floats for tiles of tr rows whose staged rows hold xc floats: ring
 // slots of (tr + 2) xc floats, channels 16 mod 64 floats apart so the four
@@ -90,8 +116,9 @@ constexpr int chan_floats(int tr, int xc) {
 // VLOAD: W % 4 == 0 and x 16-byte aligned (16-byte plane loads).
 // VSTORE: every lane's four voxels are consecutive and 16-byte aligned in y.
 // SERIES: the clamp bounds lie in [-1, 1] (series GELU).
-template <int FIXED_XC, int FIXED_TR, bool VLOAD, bool VSTORE, bool SERIES>
+template <class L, int FIXED_XC, int FIXED_TR, bool VLOAD, bool VSTORE, bool SERIES>
 __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel(Conv3dArgs a) {
+  constexpr int CI = L::CI, CO = L::CO, KSTEPS = L::KSTEPS, NT = L::NT, WS_FLOATS = L::WS_FLOATS;
   const int XC = FIXED_XC ? FIXED_XC : a.XC;
   const int TR = FIXED_TR ? FIXED_TR : a.TR;
   const int chstride = FIXED_XC ? chan_floats(FIXED_TR, FIXED_XC) : a.chstride;
@@ -104,7 +131,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
 
   // ws[s][lane][nt] = w[16 nt + lane % 16][4 (s / 27) + lane / 16][tap s % 27].
   for (int e = tid; e < WS_FLOATS; e += THREADS) {
-    const int nt = e & 3, ln = (e >> 2) & 63, st = e >> 8;
+    const int nt = e % NT, ln = (e / NT) & 63, st = e / (NT * 64);
     const int o = 16 * nt + (ln & 15), ci = 4 * (st / TAPS) + (ln >> 4);
     ws[e] = a.w[(o * CI + ci) * TAPS + (st % TAPS)];
   }
@@ -139,8 +166,8 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
     const bool contig = a.coltiles == 1;                // the tile spans whole output rows
     const int V = rows * cols, MTT = (V + 15) >> 4;     // voxels and 16-voxel blocks
     stage.init(len, tid);
-    auto src_of = [&](int dd) { return PlaneSrc{a.x, a.D, a.H, a.W, n, dd, h0, c0}; };
-    auto dst_of = [&](int dd) { return PlaneDst{xs, chstride, (dd % SLOTS) * planestride, XC}; };
+    auto src_of = [&](int dd) { return PlaneSrc<CI>{a.x, a.D, a.H, a.W, n, dd, h0, c0}; };
+    auto dst_of = [&](int dd) { return PlaneDst<CI>{xs, chstride, (dd % SLOTS) * planestride, XC}; };
 
     // Planes 0, 1, 2 of this block (every wave is past the previous block's
     // last barrier, so all slots are free).
@@ -191,17 +218,15 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
         for (int s = 0; s < KSTEPS; ++s) {
           const int tt = s % TAPS, kd = tt / 9, kh = (tt / 3) % 3, kw = tt % 3;
           const int off = (s / TAPS) * 4 * chstride + kh * XC + kw;
-          const v4f bv = *reinterpret_cast<const v4f *>(&ws[(s * 64 + lane) * NT]);
+          float bv[NT];
+          load_b<NT>(bv, &ws[(s * 64 + lane) * NT]);
           float av[MT];
 #pragma unroll
           for (int j = 0; j < MT; ++j) av[j] = xs[base[j][kd] + off];
 #pragma unroll
-          for (int j = 0; j < MT; ++j) {
-            acc[j][0] = mfma16x16x4(av[j], bv.x, acc[j][0]);
-            acc[j][1] = mfma16x16x4(av[j], bv.y, acc[j][1]);
-            acc[j][2] = mfma16x16x4(av[j], bv.z, acc[j][2]);
-            acc[j][3] = mfma16x16x4(av[j], bv.w, acc[j][3]);
-          }
+          for (int j = 0; j < MT; ++j)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[j][nt] = mfma16x16x4(av[j], bv[nt], acc[j][nt]);
         }
 
 #pragma unroll
@@ -255,10 +280,10 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
   }
 }
 
-template <int FXC, int FTR, bool VL, bool VS, bool SER>
+template <class L, int FXC, int FTR, bool VL, bool VS, bool SER>
 int launch_instance(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev,
                     hipStream_t stream) {
-  auto kern = conv3d_lrelu_add_clamp_gelu_kernel<FXC, FTR, VL, VS, SER>;
+  auto kern = conv3d_lrelu_add_clamp_gelu_kernel<L, FXC, FTR, VL, VS, SER>;
   if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds_bytes) != hipSuccess)
     return CCE_ERR_LAUNCH;
@@ -273,30 +298,34 @@ int launch_instance(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev
   return launch_status();
 }
 
-template <bool VL, bool VS>
+template <class L, bool VL, bool VS>
 int launch_series(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev,
                   hipStream_t stream) {
   const bool series = a.lo >= -1.0f && a.hi <= 1.0f;
   // 64-float staged rows in 8-row tiles (W = 64, as in the page's workload)
   // get their own instance with compile-time LDS offsets.
   if (a.XC == 64 && a.TR == 8)
-    return series ? launch_instance<64, 8, VL, VS, true>(a, lds_bytes, dev, stream)
-                  : launch_instance<64, 8, VL, VS, false>(a, lds_bytes, dev, stream);
-  return series ? launch_instance<0, 0, VL, VS, true>(a, lds_bytes, dev, stream)
-                : launch_instance<0, 0, VL, VS, false>(a, lds_bytes, dev, stream);
+    return series ? launch_instance<L, 64, 8, VL, VS, true>(a, lds_bytes, dev, stream)
+                  : launch_instance<L, 64, 8, VL, VS, false>(a, lds_bytes, dev, stream);
+  return series ? launch_instance<L, 0, 0, VL, VS, true>(a, lds_bytes, dev, stream)
+                : launch_instance<L, 0, 0, VL, VS, false>(a, lds_bytes, dev, stream);
 }
 
+template <class L>
 size_t ring_floats(int tr, int xc, int *planestride, int *chstride) {
   *planestride = plane_floats(tr, xc);
   *chstride = chan_floats(tr, xc);
-  return (size_t)CI * *chstride;
+  return (size_t)L::CI * *chstride;
 }
 
-}  // namespace
-
-int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,
-                                       const float *s, float *y, int N, int D, int H, int W,
-                                       float slope, float lo, float hi, hipStream_t stream) {
+// Tiling of one layer shape and its launch.  ALL_PATHS: the shape has
+// instances with 16-byte loads and stores, compile-time LDS offsets and the
+// polynomial GELU; otherwise the one instance with scalar loads and stores
+// and erff.
+template <class L, bool ALL_PATHS>
+int launch_layer(const float *x, const float *w, const float *b, const float *s, float *y, int N,
+                 int D, int H, int W, float slope, float lo, float hi, hipStream_t stream) {
+  constexpr size_t EXTRA = L::WS_FLOATS + 2 * L::CO;  // weights, bias and s beside the ring
   DeviceInfo dev;
   if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
   Conv3dArgs a;
@@ -314,7 +343,7 @@ int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const flo
   a.slope = slope;
   a.lo = lo;
   a.hi = hi;
-  const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  const bool vl = ALL_PATHS && (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
   const size_t budget = dev.lds_per_block / sizeof(float);
 
   // Whole rows, 8 output rows per tile if they fit; else fewer rows; else
@@ -325,8 +354,8 @@ int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const flo
   size_t ring = 0;
   for (int tr = 8; tr >= 2 && a.TR == 0; tr /= 2) {
     const int xc = vl ? ((W + 3) & ~3) : W;
-    ring = ring_floats(tr, xc, &a.planestride, &a.chstride);
-    if (WS_FLOATS + ring + 2 * CO <= budget) {
+    ring = ring_floats<L>(tr, xc, &a.planestride, &a.chstride);
+    if (EXTRA + ring <= budget) {
       a.TR = tr;
       a.TC = a.Wo;
       a.XC = xc;
@@ -337,8 +366,8 @@ int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const flo
     // Staged columns: TC + 2 rounded up to a multiple of 4.
     for (int tc = (a.Wo - 1) & ~3; tc >= 4; tc -= 4) {
       const int xc = (tc + 2 + 3) & ~3;
-      ring = ring_floats(a.TR, xc, &a.planestride, &a.chstride);
-      if (WS_FLOATS + ring + 2 * CO <= budget) {
+      ring = ring_floats<L>(a.TR, xc, &a.planestride, &a.chstride);
+      if (EXTRA + ring <= budget) {
         a.TC = tc;
         a.XC = xc;
         break;
@@ -346,7 +375,7 @@ int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const flo
     }
     if (a.TC <= 0 || a.TC >= a.Wo) return CCE_ERR_UNSUPPORTED;
   }
-  const size_t lds_bytes = (WS_FLOATS + ring + 2 * CO) * sizeof(float);
+  const size_t lds_bytes = (EXTRA + ring) * sizeof(float);
   a.rowtiles = (a.Ho + a.TR - 1) / a.TR;
   a.coltiles = (a.Wo + a.TC - 1) / a.TC;
   const long long nb = (long long)N * a.rowtiles * a.coltiles;
@@ -361,12 +390,37 @@ int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const flo
   // whole-row tiles need (TR Wo) and (Ho Wo) multiples of 4; column tiles
   // need Wo % 4 == 0 (TC is a multiple of 4).
   const bool y16 = (uintptr_t)y % 16 == 0;
-  const bool vs = y16 && (a.coltiles == 1 ? ((a.Ho * a.Wo) % 4 == 0 && (a.TR * a.Wo) % 4 == 0)
-                                          : (a.Wo % 4 == 0));
-  if (vl) return vs ? launch_series<true, true>(a, lds_bytes, dev, stream)
-                    : launch_series<true, false>(a, lds_bytes, dev, stream);
-  return vs ? launch_series<false, true>(a, lds_bytes, dev, stream)
-            : launch_series<false, false>(a, lds_bytes, dev, stream);
+  const bool vs = ALL_PATHS && y16 &&
+                  (a.coltiles == 1 ? ((a.Ho * a.Wo) % 4 == 0 && (a.TR * a.Wo) % 4 == 0) : (a.Wo % 4 == 0));
+  if constexpr (ALL_PATHS) {
+    if (vl) return vs ? launch_series<L, true, true>(a, lds_bytes, dev, stream)
+                      : launch_series<L, true, false>(a, lds_bytes, dev, stream);
+    return vs ? launch_series<L, false, true>(a, lds_bytes, dev, stream)
+              : launch_series<L, false, false>(a, lds_bytes, dev, stream);
+  } else {
+    return launch_instance<L, 0, 0, false, false, false>(a, lds_bytes, dev, stream);
+  }
+}
+
+}  // namespace
+
+int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,
+                                       const float *s, float *y, int N, int C_in, int D, int H,
+                                       int W, int C_out, float slope, float lo, float hi,
+                                       hipStream_t stream) {
+  // The page's layer, 8 -> 64 channels, with every fast path.
+  if (C_in == 8 && C_out == 64)
+    return launch_layer<Layer3<8, 64>, true>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
+  // Other layer shapes: C_in of 4, 8 or 16, C_out of 16, 32 or 64 (3 x 3 x 3);
+  // scalar loads and stores and erff.
+#define CCE_CONV3D_LAYER(CI, CO)                                                             \
+  if (C_in == CI && C_out == CO)                                                            \
+    return launch_layer<Layer3<CI, CO>, false>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
+  CCE_CONV3D_LAYER(4, 16) CCE_CONV3D_LAYER(4, 32) CCE_CONV3D_LAYER(4, 64)
+  CCE_CONV3D_LAYER(8, 16) CCE_CONV3D_LAYER(8, 32)
+  CCE_CONV3D_LAYER(16, 16) CCE_CONV3D_LAYER(16, 32) CCE_CONV3D_LAYER(16, 64)
+#undef CCE_CONV3D_LAYER
+  return CCE_ERR_UNSUPPORTED;
 }
 
 }  // namespace cce

@@ -93,9 +93,13 @@ int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y,
  * LeakyReLU(t) = t for t >= 0, slope * t otherwise; clamp to [lo, hi];
  * GELU(t) = 0.5 t (1 + erf(t / sqrt 2)) (exact, not the tanh form).
  *
- * Supported: C_in = 8, C_out = 64, k = 3, any N >= 1, D, H, W >= 3 with
- * W <= 512, lo <= hi, all three scalars finite, N*C_out*(D-2)*(H-2)*(W-2)
- * < 2^31.  Anything else returns CCE_ERR_UNSUPPORTED (or CCE_ERR_SHAPE).
+ * Supported: k = 3; the page's C_in = 8, C_out = 64 (the tuned instance:
+ * 16-byte loads and stores, polynomial GELU when [lo, hi] lies in [-1, 1])
+ * and C_in in {4, 8, 16}, C_out in {16, 32, 64} (scalar loads and stores,
+ * erff); any N >= 1, D, H, W >= 3 (rows too wide for LDS are split into
+ * column tiles); lo <= hi and all three scalars finite;
+ * N*C_out*(D-2)*(H-2)*(W-2) < 2^31.  Anything else returns
+ * CCE_ERR_UNSUPPORTED (or CCE_ERR_SHAPE / CCE_ERR_TOO_LARGE).
  */
 int conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b, const float *s,
                                 float *y, int N, int C_in, int D, int H, int W, int C_out, int k,

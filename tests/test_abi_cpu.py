@@ -81,8 +81,10 @@ def test_conv3d_validation(lib):
     assert c3(lib, s=None) == ENULL
     assert c3(lib, x=None) == ENULL
     assert c3(lib, D=2) == ESHAPE
-    assert c3(lib, C_in=4) == EUNSUP
-    assert c3(lib, W=600) == EUNSUP
+    assert c3(lib, C_in=3) == EUNSUP
+    assert c3(lib, C_in=32) == EUNSUP
+    assert c3(lib, C_out=48) == EUNSUP
+    assert c3(lib, k=5) == EUNSUP
     assert c3(lib, lo=1.0, hi=-1.0) == EUNSUP
     assert c3(lib, slope=float("nan")) == EUNSUP
     assert c3(lib, hi=float("inf")) == EUNSUP

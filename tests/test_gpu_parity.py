@@ -129,7 +129,8 @@ CONV3D_SMALL = [  # (N, D, H, W, bias)
     (3, 4, 22, 64, False),  # NULL bias, 4 row tiles of 8 (last one 4 rows)
     (1, 16, 64, 64, True),  # one image of the Conv3d workload
     (1, 4, 20, 300, True),  # rows too wide for LDS: column tiles of 76, the last one ragged
-    (1, 3, 11, 512, False),  # widest supported rows
+    (1, 3, 11, 512, False),  # 512-wide rows: 7 column tiles
+    (1, 3, 6, 700, True),   # wider still: 10 column tiles, the last ragged
 ]
 
 
@@ -142,6 +143,19 @@ def test_conv3d_small(cce, N, D, H, W, bias):
     torch.cuda.synchronize()
     ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], b, s, 0.2, -1.0, 1.0)
     assert_close(y.cpu().numpy(), ref, f"conv3d N={N} {D}x{H}x{W}")
+
+
+@pytest.mark.parametrize("C_in,C_out", [(4, 16), (4, 64), (8, 32), (16, 16), (16, 64)])
+def test_conv3d_other_layer_shapes(cce, C_in, C_out):
+    """Channel counts beyond the page's 8 -> 64 (3 x 3 x 3): scalar paths and
+    erff; 16 -> 64 leaves so little LDS beside its weights that its rows are
+    split into column tiles."""
+    p = make_inputs(CONV3D, seed=700 + C_in + C_out, N=2, C_in=C_in, D=5, H=13, W=21, C_out=C_out, k=3)
+    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, -1.0, 1.0)
+    torch.cuda.synchronize()
+    assert y.shape == (2, C_out, 3, 11, 19)
+    assert_close(y.cpu().numpy(), O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"]),
+                 f"conv3d {C_in}->{C_out}")
 
 
 def test_conv3d_other_epilogue_parameters(cce):
