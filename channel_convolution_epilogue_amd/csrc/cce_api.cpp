@@ -68,7 +68,7 @@ const char *cce_status_string(int status) {
   }
 }
 
-int cce_version(void) { return 100; }
+int cce_version(void) { return 101; }
 
 // Layer shapes the Conv2d kernel is instantiated for (see the header).
 static bool conv2d_layer_supported(int C_in, int C_out, int k) {

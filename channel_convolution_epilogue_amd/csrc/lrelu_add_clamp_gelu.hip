@@ -20,10 +20,12 @@ constexpr int THREADS = 256;
 constexpr int QPT = 4;                       // quads per thread
 constexpr int CHUNK = THREADS * QPT * 4;     // elements per workgroup
 
+// z and y may be the same buffer (in place): every element is read and then
+// written by the same thread, so they are not declared __restrict__.
 struct EltArgs {
-  const float *__restrict__ z;
+  const float *z;
   const float *__restrict__ s;
-  float *__restrict__ y;
+  float *y;
   long long S;
   int C, chunks;  // chunks per plane
   FastDiv divChunks;

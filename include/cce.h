@@ -2,15 +2,21 @@
  * cce.h -- C ABI of the fused small-channel convolution + epilogue library
  * (libcce.so, HIP kernels for AMD MI355X / gfx950).
  *
- * Three operators, each one kernel launch that reads its input and weights
- * from device memory and writes only its final output (the convolution
- * result never reaches device memory):
+ * Three fused operators, each one kernel launch that reads its input and
+ * weights from device memory and writes only its final output (the
+ * convolution result never reaches device memory):
  *
  *   conv2d_relu_hswish            Conv2d k x k (stride 1, padding 0) -> ReLU -> HardSwish
  *   conv3d_lrelu_add_clamp_gelu   Conv3d k^3 (stride 1, padding 0) -> LeakyReLU -> + s[c]
  *                                 -> clamp -> exact GELU
  *   convT2d_pool_htanh_mean_tanh  ConvTranspose2d -> MaxPool2d -> Hardtanh -> mean over
  *                                 (H, W) -> tanh
+ *
+ * and two epilogue-only operators over a convolution output computed
+ * elsewhere (the unfused paths the pages fall back to):
+ *
+ *   pool_htanh_mean_tanh          MaxPool2d -> Hardtanh -> mean over (H, W) -> tanh
+ *   lrelu_add_clamp_gelu          LeakyReLU -> + s[c] -> clamp -> exact GELU
  *
  * The operators are the three models of the POPCORNBENCH Kimi-K2.6 level-2
  * transcripts l2_p57, l2_p90 and l2_p10 (each entry point names its page).
@@ -55,7 +61,8 @@ typedef enum {
 /* Human-readable text for a cce_status value (static storage, never NULL). */
 const char *cce_status_string(int status);
 
-/* Library ABI version: 100 * major + minor. */
+/* Library ABI version: 100 * major + minor (1.1: further layer shapes for
+ * the convolutions, any pooling window and stride for the pooled tail). */
 int cce_version(void);
 
 /*

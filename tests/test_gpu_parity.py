@@ -321,6 +321,20 @@ def test_epilogue_fp32_accuracy(cce, slope, lo, hi):
     assert err.max() < 2e-7, f"max excess error {err.max():.3e} (slope {slope}, clamp [{lo}, {hi}])"
 
 
+@pytest.mark.parametrize("S", [4096 * 3 + 12, 999])
+def test_elementwise_tail_in_place(cce, S):
+    """y may be z: the in-place call matches the out-of-place one bit for bit
+    (16-byte path with a ragged last chunk, and the scalar path)."""
+    p = make_inputs(TAIL_GELU, seed=520 + S, N=2, C=3, D=1, H=1, W=S)
+    z = dev(p["z"])
+    ref = cce.lrelu_add_clamp_gelu(z, dev(p["s"]), 0.2, -1.0, 1.0)
+    zz = z.clone()
+    out = cce.lrelu_add_clamp_gelu(zz, dev(p["s"]), 0.2, -1.0, 1.0, out=zz)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == zz.data_ptr()
+    assert torch.equal(zz, ref)
+
+
 def test_elementwise_tail_workload_sampled(cce):
     shape, p = workload_inputs("lrelu_add_clamp_gelu_n128", seed=0)
     y = cce.lrelu_add_clamp_gelu(dev(p["z"]), dev(p["s"]), shape["slope"], shape["lo"], shape["hi"])
