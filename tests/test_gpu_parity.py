@@ -350,3 +350,52 @@ def test_elementwise_tail_workload_sampled(cce):
     assert_close(yh.reshape(-1)[idx[:20000]], ref, "elementwise tail n128 sampled")
     head = O.lrelu_add_clamp_gelu_array(p["z"][:1], p["s"])
     assert_close(yh[:1], head, "elementwise tail n128 first image")
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture
+# ---------------------------------------------------------------------------
+
+def test_graph_capture_replays_match_eager(cce):
+    """All five operators captured in one HIP graph (torch.cuda.graph) and
+    replayed three times, with eager work and a synchronisation between the
+    replays: every replay matches the eager results bit for bit.  The calls
+    allocate nothing and issue no memset, so they are capturable; the ConvT
+    workspace is passed in, zeroed before capture, and left zeroed by the
+    kernel."""
+    p2 = make_inputs(CONV2D, seed=801, N=2, C_in=8, H=21, W=30, C_out=64, k=3)
+    p3 = make_inputs(CONV3D, seed=802, N=1, C_in=8, D=5, H=12, W=16, C_out=64, k=3)
+    pt = make_inputs(CONVT, seed=803, N=2, C_in=64, H=18, W=20, C_out=64, k=3)
+    pp = make_inputs(TAIL_POOL, seed=804, N=2, C=3, H=16, W=20)
+    pg = make_inputs(TAIL_GELU, seed=805, N=2, C=4, D=2, H=5, W=8)
+    d2 = {k: dev(v) for k, v in p2.items()}
+    d3 = {k: dev(v) for k, v in p3.items()}
+    dt = {k: dev(v) for k, v in pt.items()}
+    zp, zg, sg = dev(pp["z"]), dev(pg["z"]), dev(pg["s"])
+    ws = torch.zeros(cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(2, 64, 18, 20, 64),
+                     dtype=torch.uint8, device="cuda")
+
+    def run(outs):
+        cce.conv2d_relu_hswish(d2["x"], d2["w"], d2["b"], out=outs[0])
+        cce.conv3d_lrelu_add_clamp_gelu(d3["x"], d3["w"], d3["b"], d3["s"], 0.2, -1.0, 1.0, out=outs[1])
+        cce.convT2d_pool_htanh_mean_tanh(dt["x"], dt["w"], dt["b"], out=outs[2], workspace=ws)
+        cce.pool_htanh_mean_tanh(zp, out=outs[3])
+        cce.lrelu_add_clamp_gelu(zg, sg, 0.2, -1.0, 1.0, out=outs[4])
+
+    shapes = [(2, 64, 19, 28), (1, 64, 3, 10, 14), (2, 64, 1, 1), (2, 3, 1, 1), tuple(zg.shape)]
+    eager = [torch.empty(sh, device="cuda") for sh in shapes]
+    run(eager)
+    torch.cuda.synchronize()
+    outs = [torch.empty(sh, device="cuda") for sh in shapes]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(outs)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), f"replay {rep}, operator {i}"
+    assert_close(eager[0].cpu().numpy(), O.conv2d_relu_hswish(p2["x"], p2["w"], p2["b"]), "graph conv2d")
