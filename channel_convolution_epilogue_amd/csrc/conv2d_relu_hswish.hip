@@ -7,15 +7,16 @@
 //    output channels, K = 8 channels x 9 taps = 72.  Packed fp32 VALU math is
 //    not used, so the matrix cores are the only units that reach the fp32
 //    peak; the contraction is dense enough (72 x 64 per pixel) to feed them.
-//  * The unit of work is one wave's strip: 16 output columns by 2 output rows
-//    of one image, all 64 channels (two 16-pixel MFMA blocks).  Each wave
-//    stages its strip's input window (8 channels x 4 rows x 24 columns) in a
-//    slice of LDS of its own, so no wave ever waits for another's data.  The
-//    next strip's window is loaded into registers while the current strip's
-//    MFMAs run, and written to the wave's slice after them.
+//  * The unit of work is one wave's strip: 16 output columns of one output
+//    row of one image, all 64 channels (one 16-pixel MFMA block per channel
+//    block).  Each wave stages its strip's input window (8 channels x 3 rows
+//    x 24 columns) in a slice of LDS of its own, so no wave ever waits for
+//    another's data.  The next strip's window is loaded into registers while
+//    the current strip's MFMAs run, and written to the wave's slice after
+//    them.
 //  * Strips are dealt in rounds, strip index fastest: in one round the 16
 //    waves of a workgroup take 16 consecutive strips, i.e. whole rows of the
-//    output (8 strips cover 126 columns), and write 4 full rows of every
+//    output (8 strips cover 126 columns), and write 2 full rows of every
 //    channel plane.  One barrier per round keeps the waves in step, so that
 //    the 64-byte pieces that neighbouring waves write into one 128-byte line
 //    reach the L2 together.  Measured on MI355X: without it, partly written
@@ -126,18 +127,6 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
 
-  // B operand of K-step s = (half, kh, kw) for all four 16-channel blocks:
-  // ws[s][lane][nt] = w[16 nt + lane % 16][4 half + lane / 16][kh][kw].
-  for (int e = tid; e < WS_FLOATS; e += THREADS) {
-    const int nt = e % NT, ln = (e / NT) & 63, st = e / (NT * 64);
-    const int o = 16 * nt + (ln & 15), ci = 4 * (st / TAPS) + (ln >> 4);
-    ws[e] = a.w[(o * CI + ci) * TAPS + (st % TAPS)];
-  }
-  float bias[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
-  __syncthreads();  // the only workgroup barrier: waves are independent from here on
-
   // The hardware hands workgroups to the 8 XCDs in turn (b -> XCD b % 8); the
   // remap gives each XCD a contiguous block of each round's strips, so one L2
   // collects long runs of every output plane.  (gridDim.x is a multiple of 8.)
@@ -203,9 +192,23 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
     }
   };
 
+  // The first window's loads go out before the weight staging, so the two
+  // latencies overlap.
   Strip cur = decode(item);
   load(cur);
+
+  // B operand of K-step s = (half, kh, kw) for all four 16-channel blocks:
+  // ws[s][lane][nt] = w[16 nt + lane % 16][4 half + lane / 16][kh][kw].
+  for (int e = tid; e < WS_FLOATS; e += THREADS) {
+    const int nt = e % NT, ln = (e / NT) & 63, st = e / (NT * 64);
+    const int o = 16 * nt + (ln & 15), ci = 4 * (st / TAPS) + (ln >> 4);
+    ws[e] = a.w[(o * CI + ci) * TAPS + (st % TAPS)];
+  }
+  float bias[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
   put();
+  __syncthreads();  // weights in place; from here on only the per-round barrier
 
   for (;;) {
     const bool more = first + step < a.items;  // workgroup-uniform
@@ -362,18 +365,20 @@ int launch_layer(const float *x, const float *w, const float *b, float *y, int N
 
 int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
                               int C_in, int H, int W, int C_out, int k, hipStream_t stream) {
-  // The page's layer, 8 -> 64 channels, 3 x 3: strips of 2 rows x 16 columns
-  // and every 16-byte path.  Measured on MI355X at N = 128 (ms): 2 x 16:
-  // 0.199, 1 x 16: 0.204, 1 x 32: 0.211, 3 x 16: 0.294 (spills); 16-wave
-  // workgroups 0.195 against 0.199 for 8-wave ones.
+  // The page's layer, 8 -> 64 channels, 3 x 3: strips of 1 row x 16 columns
+  // and every 16-byte path.  Measured on MI355X with 16-wave workgroups (ms):
+  // 1 x 16: 0.194 at N = 128 and 0.0184 at N = 8 (two rounds per workgroup,
+  // so the first round's stores overlap the second round's MFMAs); 2 x 16:
+  // 0.196 and 0.0197.  With 8-wave workgroups 2 x 16 was best (0.199), 1 x 32
+  // 0.211, 3 x 16 0.294 (spills).
   if (C_in == 8 && C_out == 64 && k == 3)
-    return launch_layer<StripGeo<2, 1, 8, 64, 3>, true>(x, w, b, y, N, H, W, stream);
+    return launch_layer<StripGeo<1, 1, 8, 64, 3>, true>(x, w, b, y, N, H, W, stream);
   // Other layer shapes whose weights and 16 wave windows fit in LDS: C_in of
   // 4, 8 or 16, C_out of 16, 32 or 64, 1 x 1, 3 x 3 or 5 x 5 kernels (5 x 5
   // up to 8 input channels); scalar loads and stores.
 #define CCE_CONV2D_LAYER(CI, CO, KS)                                                        \
   if (C_in == CI && C_out == CO && k == KS)                                                \
-    return launch_layer<StripGeo<2, 1, CI, CO, KS>, false>(x, w, b, y, N, H, W, stream);
+    return launch_layer<StripGeo<1, 1, CI, CO, KS>, false>(x, w, b, y, N, H, W, stream);
 #define CCE_CONV2D_LAYERS_CO(CI, KS) \
   CCE_CONV2D_LAYER(CI, 16, KS) CCE_CONV2D_LAYER(CI, 32, KS) CCE_CONV2D_LAYER(CI, 64, KS)
   CCE_CONV2D_LAYERS_CO(4, 1) CCE_CONV2D_LAYERS_CO(8, 1) CCE_CONV2D_LAYERS_CO(16, 1)
