@@ -68,7 +68,7 @@ const char *cce_status_string(int status) {
   }
 }
 
-int cce_version(void) { return 101; }
+int cce_version(void) { return 102; }
 
 // Layer shapes the Conv2d kernel is instantiated for (see the header).
 static bool conv2d_layer_supported(int C_in, int C_out, int k) {
@@ -118,7 +118,8 @@ static int convT_check_shape(int N, int C_in, int H, int W, int C_out, int k, in
   const long long Ho = (long long)(H - 1) * stride - 2LL * pad + k;
   const long long Wo = (long long)(W - 1) * stride - 2LL * pad + k;
   if (Ho < pool_k || Wo < pool_k) return CCE_ERR_SHAPE;
-  if (C_in != 64 || C_out != 64 || k != 3 || stride != 1 || pad != 1 || pool_k != 2 || pool_s != 2)
+  if (!cce::convT_layer_supported(C_in, C_out) || k != 3 || stride != 1 || pad != 1 || pool_k != 2 ||
+      pool_s != 2)
     return CCE_ERR_UNSUPPORTED;
   if ((long long)N * C_in * H * W >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
   return CCE_OK;
@@ -128,7 +129,7 @@ size_t convT2d_pool_htanh_mean_tanh_workspace_bytes(int N, int C_in, int H, int 
                                                     int k, int stride, int pad, int pool_k,
                                                     int pool_s) {
   if (convT_check_shape(N, C_in, H, W, C_out, k, stride, pad, pool_k, pool_s) != CCE_OK) return 0;
-  return cce::convT_workspace_bytes(N, H, W);
+  return cce::convT_workspace_bytes(N, C_in, H, W, C_out);
 }
 
 int convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b, float *y, int N,
@@ -141,10 +142,10 @@ int convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b,
   if (!is_finite_f(htanh_lo) || !is_finite_f(htanh_hi) || htanh_lo > htanh_hi) return CCE_ERR_UNSUPPORTED;
   if (!aligned4(x) || !aligned4(w) || !aligned4(y) || (b && !aligned4(b))) return CCE_ERR_ALIGN;
   if (!workspace || ((uintptr_t)workspace & 255u) != 0 ||
-      workspace_bytes < cce::convT_workspace_bytes(N, H, W))
+      workspace_bytes < cce::convT_workspace_bytes(N, C_in, H, W, C_out))
     return CCE_ERR_WORKSPACE;
-  return cce::launch_convT2d_pool_htanh_mean_tanh(x, w, b, y, N, H, W, htanh_lo, htanh_hi,
-                                                  workspace, (hipStream_t)stream);
+  return cce::launch_convT2d_pool_htanh_mean_tanh(x, w, b, y, N, C_in, H, W, C_out, htanh_lo,
+                                                  htanh_hi, workspace, (hipStream_t)stream);
 }
 
 int pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, int pool_k,

@@ -23,6 +23,52 @@ __device__ __forceinline__ v4f mfma16x16x4(float a, float b, v4f c) {
 
 __device__ __forceinline__ v4f splat4(float v) { return v4f{v, v, v, v}; }
 
+// Stages a [CO][CI][TAPS] convolution weight (the torch layout) into LDS in
+// MFMA B-operand order: K-step s covers input channels 4 (s / TAPS) .. + 3 at
+// tap s % TAPS, and
+//   ws[(s * 64 + lane) * NT + nt] = w[16 nt + lane % 16][4 (s / TAPS) + lane / 16][s % TAPS].
+// Consecutive threads read consecutive floats of w (16-byte loads when w is
+// 16-byte aligned), so each wave's load touches two or eight cache lines;
+// the reordering happens on the LDS side.  Needs CI % 4 == 0, CO % 16 == 0.
+template <int CI, int CO, int TAPS, int THREADS>
+__device__ __forceinline__ void stage_weights_b(float *ws, const float *__restrict__ w, int tid) {
+  constexpr int NT = CO / 16, TOTAL = CO * CI * TAPS;
+  static_assert(CI % 4 == 0 && CO % 16 == 0, "whole K-steps and channel blocks");
+  auto place = [&](int e, float v) {
+    const int o = e / (CI * TAPS), r = e - o * (CI * TAPS);
+    const int ci = r / TAPS, tap = r - ci * TAPS;
+    const int s = (ci >> 2) * TAPS + tap, lane = ((ci & 3) << 4) | (o & 15);
+    ws[(s * 64 + lane) * NT + (o >> 4)] = v;
+  };
+  if ((reinterpret_cast<uintptr_t>(w) & 15) == 0) {
+    for (int q = tid; q < TOTAL / 4; q += THREADS) {
+      const v4f v = reinterpret_cast<const v4f *>(w)[q];
+      place(4 * q, v.x);
+      place(4 * q + 1, v.y);
+      place(4 * q + 2, v.z);
+      place(4 * q + 3, v.w);
+    }
+  } else {
+    for (int e = tid; e < TOTAL; e += THREADS) place(e, w[e]);
+  }
+}
+
+// A lane's MFMA B operands of one K-step for NT 16-column channel blocks,
+// stored contiguously in LDS: one 16-, 8- or 4-byte LDS read.
+template <int NT>
+__device__ __forceinline__ void load_b(float (&bv)[NT], const float *p) {
+  if constexpr (NT == 4) {
+    const v4f v = *reinterpret_cast<const v4f *>(p);
+    bv[0] = v.x, bv[1] = v.y, bv[2] = v.z, bv[3] = v.w;
+  } else if constexpr (NT == 2) {
+    const float2 v = *reinterpret_cast<const float2 *>(p);
+    bv[0] = v.x, bv[1] = v.y;
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bv[nt] = p[nt];
+  }
+}
+
 __device__ __forceinline__ float clampf(float v, float lo, float hi) {
   return fminf(fmaxf(v, lo), hi);
 }

@@ -18,21 +18,23 @@ struct DeviceInfo {
 };
 int current_device_info(DeviceInfo *info);  // CCE_OK or CCE_ERR_LAUNCH
 
-// Conv2d 3x3 (8 -> 64) + ReLU + HardSwish.  Arguments already validated.
+// Conv2d (page layer 3x3, 8 -> 64) + ReLU + HardSwish.  Arguments already validated.
 int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
                               int C_in, int H, int W, int C_out, int k, hipStream_t stream);
 
-// Conv3d 3x3x3 (8 -> 64) + LeakyReLU + add + clamp + GELU.  Validated.
+// Conv3d 3x3x3 (page layer 8 -> 64) + LeakyReLU + add + clamp + GELU.  Validated.
 int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,
                                        const float *s, float *y, int N, int C_in, int D, int H,
                                        int W, int C_out, float slope, float lo, float hi,
                                        hipStream_t stream);
 
-// ConvTranspose2d 3x3 s1 p1 (64 -> 64) + MaxPool 2x2 + Hardtanh + mean + tanh.
-size_t convT_workspace_bytes(int N, int H, int W);
+// ConvTranspose2d 3x3 s1 p1 (C_in % 8 == 0, C_out in {16, 32, 64}) + MaxPool
+// 2x2 + Hardtanh + mean + tanh.
+bool convT_layer_supported(int C_in, int C_out);
+size_t convT_workspace_bytes(int N, int C_in, int H, int W, int C_out);
 int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b, float *y,
-                                        int N, int H, int W, float lo, float hi, void *workspace,
-                                        hipStream_t stream);
+                                        int N, int C_in, int H, int W, int C_out, float lo, float hi,
+                                        void *workspace, hipStream_t stream);
 
 // Epilogue-only operators over a precomputed convolution output.
 int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, int pool_k,

@@ -97,22 +97,6 @@ struct Strip {
   int n, r0, c0;
 };
 
-// A lane's B operands of one K-step for all NT channel blocks: one 16-, 8- or
-// 4-byte LDS read.
-template <int NT>
-__device__ __forceinline__ void load_b(float (&bv)[NT], const float *p) {
-  if constexpr (NT == 4) {
-    const v4f v = *reinterpret_cast<const v4f *>(p);
-    bv[0] = v.x, bv[1] = v.y, bv[2] = v.z, bv[3] = v.w;
-  } else if constexpr (NT == 2) {
-    const float2 v = *reinterpret_cast<const float2 *>(p);
-    bv[0] = v.x, bv[1] = v.y;
-  } else {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bv[nt] = p[nt];
-  }
-}
-
 // VLOAD: W % 4 == 0 and x 16-byte aligned (16-byte window loads).
 // VSTORE: P % 4 == 0 and y 16-byte aligned (16-byte result stores).
 template <class GEO, bool VLOAD, bool VSTORE>
@@ -197,13 +181,8 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   Strip cur = decode(item);
   load(cur);
 
-  // B operand of K-step s = (half, kh, kw) for all four 16-channel blocks:
-  // ws[s][lane][nt] = w[16 nt + lane % 16][4 half + lane / 16][kh][kw].
-  for (int e = tid; e < WS_FLOATS; e += THREADS) {
-    const int nt = e % NT, ln = (e / NT) & 63, st = e / (NT * 64);
-    const int o = 16 * nt + (ln & 15), ci = 4 * (st / TAPS) + (ln >> 4);
-    ws[e] = a.w[(o * CI + ci) * TAPS + (st % TAPS)];
-  }
+  // B operand of K-step s = (channel quad, kh, kw) for all NT 16-channel blocks.
+  stage_weights_b<CI, CO, TAPS, THREADS>(ws, a.w, tid);
   float bias[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;

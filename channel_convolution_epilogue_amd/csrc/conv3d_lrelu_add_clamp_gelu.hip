@@ -86,22 +86,6 @@ struct PlaneDst {
   }
 };
 
-// A lane's B operands of one K-step for all NT channel blocks: one 16-, 8- or
-// 4-byte LDS read.
-template <int NT>
-__device__ __forceinline__ void load_b(float (&bv)[NT], const float *p) {
-  if constexpr (NT == 4) {
-    const v4f v = *reinterpret_cast<const v4f *>(p);
-    bv[0] = v.x, bv[1] = v.y, bv[2] = v.z, bv[3] = v.w;
-  } else if constexpr (NT == 2) {
-    const float2 v = *reinterpret_cast<const float2 *>(p);
-    bv[0] = v.x, bv[1] = v.y;
-  } else {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bv[nt] = p[nt];
-  }
-}
-
 // LDS floats for tiles of tr rows whose staged rows hold xc floats: ring
 // slots of (tr + 2) xc floats, channels 16 mod 64 floats apart so the four
 // lane groups of an A read (four channels) start on four different quarters
@@ -130,11 +114,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
   const int g = lane >> 4, col = lane & 15;
 
   // ws[s][lane][nt] = w[16 nt + lane % 16][4 (s / 27) + lane / 16][tap s % 27].
-  for (int e = tid; e < WS_FLOATS; e += THREADS) {
-    const int nt = e % NT, ln = (e / NT) & 63, st = e / (NT * 64);
-    const int o = 16 * nt + (ln & 15), ci = 4 * (st / TAPS) + (ln >> 4);
-    ws[e] = a.w[(o * CI + ci) * TAPS + (st % TAPS)];
-  }
+  stage_weights_b<CI, CO, TAPS, THREADS>(ws, a.w, tid);
   // Bias and the added per-channel term, read from LDS when needed (fewer
   // live registers): ep[c] = b[c], ep[64 + c] = s[c].
   float *ep = xs + CI * chstride;

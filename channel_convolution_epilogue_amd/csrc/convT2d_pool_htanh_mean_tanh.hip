@@ -1,8 +1,9 @@
-// ConvTranspose2d 3x3, stride 1, padding 1, 64 -> 64 channels, + bias ->
+// ConvTranspose2d 3x3, stride 1, padding 1, C_in -> C_out channels, + bias ->
 // MaxPool2d(2, 2) -> Hardtanh[lo, hi] -> mean over (H, W) -> tanh, fused in one
-// gfx950 kernel (POPCORNBENCH Kimi-K2.6 l2_p10).  The 64 x H x W conv result
-// and the pooled map never reach memory; each workgroup leaves 64 partial
-// sums and the last workgroup of an image writes y[n, 0..63].
+// gfx950 kernel (POPCORNBENCH Kimi-K2.6 l2_p10, whose layer is 64 -> 64).  The
+// C_out x H x W conv result and the pooled map never reach memory; each
+// workgroup leaves C_out partial sums and the last workgroup of an image
+// writes y[n, 0..C_out-1].
 //
 // Algebra (l2_p10's derivation of the stride-1 transposed conv): with
 // padding 1, output pixel (h, w) gathers x[i, h + 1 - kh, w + 1 - kw] *
@@ -12,11 +13,12 @@
 // are applied when the weight is staged into LDS.
 //
 // Design:
-//  * Implicit GEMM on the fp32 matrix cores: M = conv-output pixels, N = 64
-//    output channels, K = 64 channels x 9 taps = 576.  A tile is 16 x 32
-//    conv pixels (8 x 16 pooling windows) of one image; K is walked in 8
-//    chunks of 8 input channels whose input halo tile (18 x 34) and weight
-//    slice (8 x 9 x 64) are staged in LDS.
+//  * Implicit GEMM on the fp32 matrix cores: M = conv-output pixels, N =
+//    C_out output channels (16, 32 or 64: one to four 16-column MFMA
+//    blocks), K = C_in channels x 9 taps (576 for the page's layer).  A tile
+//    is 16 x 32 conv pixels (8 x 16 pooling windows) of one image; K is
+//    walked in C_in / 8 chunks of 8 input channels whose input halo tile
+//    (18 x 34) and weight slice (8 x 9 x C_out) are staged in LDS.
 //  * The M order puts the four pixels of one 2 x 2 pooling window on four
 //    consecutive M rows, which the matrix core returns in one lane's four
 //    accumulator registers: the max-pool is three in-lane max operations.
@@ -33,20 +35,29 @@
 namespace cce {
 namespace {
 
-constexpr int CI = 64, CO = 64, NT = CO / 16;
 constexpr int WAVES = 4, THREADS = 64 * WAVES;
 constexpr int TH = 16, TW = 32;             // conv-output pixels per tile
 constexpr int PTH = TH / 2, PTW = TW / 2;   // pooling windows per tile
-constexpr int CC = 8, NCHUNK = CI / CC;     // input channels per K chunk
+constexpr int CC = 8;                       // input channels per K chunk
 constexpr int XR = TH + 2, XC = TW + 2;     // input halo tile rows / cols
 constexpr int XRS = 40;                     // LDS row stride: 8 (mod 64) banks between rows
 constexpr int XCS = XR * XRS;               // 720 = 16 (mod 64): lane groups 16 banks apart
 constexpr int XOFF = 3;                     // LDS column of input column w0 - 1
 constexpr int XS_FLOATS = CC * XCS;
-constexpr int WS_FLOATS = (CC / 4) * 9 * 64 * NT;
 constexpr int MT = 8;                       // 16-pixel blocks per wave
 
 static_assert(XOFF + XC <= XRS, "halo row fits the LDS row");
+
+// Output-channel geometry: NT 16-column MFMA blocks; the weight slice of one
+// K chunk holds (CC / 4) x 9 x 64 lanes x NT floats.
+template <int CO_>
+struct OutCh {
+  static constexpr int CO = CO_, NT = CO / 16;
+  static constexpr int WS_FLOATS = (CC / 4) * 9 * 64 * NT;
+  static constexpr int W4_PER_CHUNK = WS_FLOATS / 4;
+  static constexpr int W4_PT = (W4_PER_CHUNK + THREADS - 1) / THREADS;
+  static_assert(CO == 16 || CO == 32 || CO == 64, "C_out is 16, 32 or 64");
+};
 
 struct ConvTArgs {
   const float *__restrict__ x;
@@ -54,8 +65,9 @@ struct ConvTArgs {
   const float *__restrict__ b;
   float *__restrict__ y;
   unsigned *tickets;  // [N] per-image completion counters (zero between calls)
-  float *partials;    // [N][tiles_per_image][64]
-  const float *wprep; // prepared weight, NCHUNK x WS_FLOATS
+  float *partials;    // [N][tiles_per_image][C_out]
+  const float *wprep; // prepared weight, nchunk x WS_FLOATS
+  int C_in, nchunk;   // nchunk = C_in / CC
   int H, W, PH, PW;
   int tiles_x, tiles_per_image;
   float lo, hi, inv_count;
@@ -66,8 +78,6 @@ struct ConvTArgs {
 // each (channel, row) are four-aligned in the image (w0 % 32 == 0, W % 4 == 0)
 // and land on four-aligned LDS columns (XOFF + 1 = 4); the two halo columns
 // are single floats.
-constexpr int W4_PER_CHUNK = WS_FLOATS / 4;                        // 1152
-constexpr int W4_PT = (W4_PER_CHUNK + THREADS - 1) / THREADS;      // 5
 constexpr int XQ = TW / 4;                                         // 8 float4 per row
 constexpr int X4_PER_CHUNK = CC * XR * XQ;                         // 1152
 constexpr int X4_PT = (X4_PER_CHUNK + THREADS - 1) / THREADS;      // 5
@@ -75,8 +85,9 @@ constexpr int XH_PER_CHUNK = CC * XR * 2;                          // 288 halo f
 constexpr int XH_PT = (XH_PER_CHUNK + THREADS - 1) / THREADS;      // 2
 static_assert(XOFF + 1 == 4, "interior columns start 16-byte aligned in LDS");
 
+template <class OC>
 struct ChunkRegs {
-  v4f w4[W4_PT];
+  v4f w4[OC::W4_PT];
   v4f x4[X4_PT];
   float xh[XH_PT];
 };
@@ -84,16 +95,16 @@ struct ChunkRegs {
 // Global -> registers for channel chunk c (issued a whole chunk ahead of use).
 // VEC: W % 4 == 0 and x 16-byte aligned, so each interior quad is one aligned
 // 16-byte load that is either wholly inside the row or wholly past its end.
-template <bool VEC>
+template <class OC, bool VEC>
 __device__ __forceinline__ void load_chunk(const ConvTArgs &a, int n, int c, int h0, int w0, int tid,
-                                           ChunkRegs &r) {
-  const v4f *wsrc = reinterpret_cast<const v4f *>(a.wprep) + (size_t)c * W4_PER_CHUNK;
+                                           ChunkRegs<OC> &r) {
+  const v4f *wsrc = reinterpret_cast<const v4f *>(a.wprep) + (size_t)c * OC::W4_PER_CHUNK;
 #pragma unroll
-  for (int j = 0; j < W4_PT; ++j) {
+  for (int j = 0; j < OC::W4_PT; ++j) {
     const int i = tid + j * THREADS;
-    if (i < W4_PER_CHUNK) r.w4[j] = wsrc[i];
+    if (i < OC::W4_PER_CHUNK) r.w4[j] = wsrc[i];
   }
-  const float *xc = a.x + ((size_t)n * CI + CC * c) * a.H * a.W;
+  const float *xc = a.x + ((size_t)n * a.C_in + CC * c) * a.H * a.W;
 #pragma unroll
   for (int j = 0; j < X4_PT; ++j) {
     const int i = tid + j * THREADS;
@@ -131,11 +142,12 @@ __device__ __forceinline__ void load_chunk(const ConvTArgs &a, int n, int c, int
 }
 
 // Registers -> LDS.
-__device__ __forceinline__ void store_chunk(float *xs, float *ws, int tid, const ChunkRegs &r) {
+template <class OC>
+__device__ __forceinline__ void store_chunk(float *xs, float *ws, int tid, const ChunkRegs<OC> &r) {
 #pragma unroll
-  for (int j = 0; j < W4_PT; ++j) {
+  for (int j = 0; j < OC::W4_PT; ++j) {
     const int i = tid + j * THREADS;
-    if (i < W4_PER_CHUNK) reinterpret_cast<v4f *>(ws)[i] = r.w4[j];
+    if (i < OC::W4_PER_CHUNK) reinterpret_cast<v4f *>(ws)[i] = r.w4[j];
   }
 #pragma unroll
   for (int j = 0; j < X4_PT; ++j) {
@@ -157,25 +169,28 @@ __device__ __forceinline__ void store_chunk(float *xs, float *ws, int tid, const
   }
 }
 
-// Weight preparation (once per call, 36,864 floats): the flipped, channel-
-// swapped kernel in exactly the LDS B-operand order of every chunk,
+// Weight preparation (once per call, C_in x C_out x 9 floats): the flipped,
+// channel-swapped kernel in exactly the LDS B-operand order of every chunk,
 //   wprep[c][cb][tap'][lane][nt] = W[8c + 4cb + lane/16][16nt + lane%16][8 - tap'],
 // where tap' = 3 kh' + kw' and W's tap index 3 kh + kw = 8 - tap'.
+template <class OC>
 __global__ __launch_bounds__(THREADS) void convT_prepare_weight_kernel(const float *__restrict__ w,
-                                                                      float *__restrict__ wprep) {
+                                                                      float *__restrict__ wprep,
+                                                                      int total) {
   const int p = blockIdx.x * THREADS + threadIdx.x;
-  if (p >= NCHUNK * WS_FLOATS) return;
-  const int nt = p & 3, lane = (p >> 2) & 63, rest = p >> 8;  // rest = (c * 2 + cb) * 9 + tap
-  const int tap = rest % 9, ccb = rest / 9;                    // ccb = c * 2 + cb
+  if (p >= total) return;
+  const int nt = p % OC::NT, lane = (p / OC::NT) & 63, rest = p / (OC::NT * 64);
+  const int tap = rest % 9, ccb = rest / 9;  // rest = (c * 2 + cb) * 9 + tap, ccb = c * 2 + cb
   const int ci = 4 * ccb + (lane >> 4), o = 16 * nt + (lane & 15);
-  wprep[p] = w[((size_t)ci * CO + o) * 9 + (8 - tap)];
+  wprep[p] = w[((size_t)ci * OC::CO + o) * 9 + (8 - tap)];
 }
 
-template <bool VEC>
+template <class OC, bool VEC>
 __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kernel(ConvTArgs a) {
+  constexpr int CO = OC::CO, NT = OC::NT;
   __shared__ __attribute__((aligned(16))) float xs[XS_FLOATS];
-  __shared__ __attribute__((aligned(16))) float ws[WS_FLOATS];
-  __shared__ float red[WAVES][64];
+  __shared__ __attribute__((aligned(16))) float ws[OC::WS_FLOATS];
+  __shared__ float red[THREADS];  // [WAVES][CO], then [THREADS / CO][CO]
   __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -196,35 +211,33 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = splat4(0.0f);
 
-  ChunkRegs r;
-  load_chunk<VEC>(a, n, 0, h0, w0, tid, r);
+  ChunkRegs<OC> r;
+  load_chunk<OC, VEC>(a, n, 0, h0, w0, tid, r);
   store_chunk(xs, ws, tid, r);
   __syncthreads();
 
 #pragma unroll 1
-  for (int c = 0; c < NCHUNK; ++c) {
+  for (int c = 0; c < a.nchunk; ++c) {
     // Next chunk's global loads are in flight while this chunk's MFMAs run.
-    if (c + 1 < NCHUNK) load_chunk<VEC>(a, n, c + 1, h0, w0, tid, r);
+    if (c + 1 < a.nchunk) load_chunk<OC, VEC>(a, n, c + 1, h0, w0, tid, r);
 #pragma unroll
     for (int cb = 0; cb < CC / 4; ++cb) {
 #pragma unroll
       for (int tap = 0; tap < 9; ++tap) {
         const int kh = tap / 3, kw = tap % 3;
-        const v4f bv = *reinterpret_cast<const v4f *>(&ws[((cb * 9 + tap) * 64 + lane) * NT]);
+        float bv[NT];
+        load_b<NT>(bv, &ws[((cb * 9 + tap) * 64 + lane) * NT]);
         float av[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           av[mt] = xs[abase + cb * 4 * XCS + (2 * (mt >> 2) + kh) * XRS + 8 * (mt & 3) + kw];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][0] = mfma16x16x4(av[mt], bv.x, acc[mt][0]);
-          acc[mt][1] = mfma16x16x4(av[mt], bv.y, acc[mt][1]);
-          acc[mt][2] = mfma16x16x4(av[mt], bv.z, acc[mt][2]);
-          acc[mt][3] = mfma16x16x4(av[mt], bv.w, acc[mt][3]);
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x4(av[mt], bv[nt], acc[mt][nt]);
       }
     }
-    if (c + 1 < NCHUNK) {
+    if (c + 1 < a.nchunk) {
       __syncthreads();  // every wave is done reading chunk c
       store_chunk(xs, ws, tid, r);
       __syncthreads();
@@ -236,7 +249,9 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
   float bias[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
-  float sum[NT] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float sum[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) sum[nt] = 0.0f;
   const int ph0 = ty * PTH, pw0 = tx * PTW;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -257,12 +272,12 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
   }
   if (g == 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) red[wave][16 * nt + col] = sum[nt];
+    for (int nt = 0; nt < NT; ++nt) red[wave * CO + 16 * nt + col] = sum[nt];
   }
   __syncthreads();
-  if (tid < 64) {
-    const float tot = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-    __hip_atomic_store(&a.partials[((size_t)n * a.tiles_per_image + ti) * 64 + tid], tot,
+  if (tid < CO) {
+    const float tot = ((red[tid] + red[CO + tid]) + red[2 * CO + tid]) + red[3 * CO + tid];
+    __hip_atomic_store(&a.partials[((size_t)n * a.tiles_per_image + ti) * CO + tid], tot,
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
@@ -277,17 +292,20 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
 
   // Last workgroup of image n: all partials of the image are visible.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  constexpr int PARTS = THREADS / CO;  // threads per output channel
   {
-    const int o = tid & 63, part = tid >> 6;
-    const float *pp = a.partials + (size_t)n * a.tiles_per_image * 64 + o;
+    const int o = tid % CO, part = tid / CO;
+    const float *pp = a.partials + (size_t)n * a.tiles_per_image * CO + o;
     float s = 0.0f;
-    for (int t = part; t < a.tiles_per_image; t += WAVES)
-      s += __hip_atomic_load(pp + (size_t)t * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    red[part][o] = s;
+    for (int t = part; t < a.tiles_per_image; t += PARTS)
+      s += __hip_atomic_load(pp + (size_t)t * CO, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    red[part * CO + o] = s;
   }
   __syncthreads();
-  if (tid < 64) {
-    const float tot = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  if (tid < CO) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int part = 0; part < PARTS; ++part) tot += red[part * CO + tid];
     a.y[(size_t)n * CO + tid] = tanhf(tot * a.inv_count);
   }
   if (tid == 0)
@@ -295,7 +313,6 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
 }
 
 constexpr size_t kTicketAlign = 256;
-constexpr size_t kWprepBytes = (size_t)NCHUNK * WS_FLOATS * sizeof(float);  // 147,456
 
 void convT_tiles(int H, int W, int *tiles_x, int *tiles_per_image) {
   const int PH = H / 2, PW = W / 2;
@@ -303,24 +320,55 @@ void convT_tiles(int H, int W, int *tiles_x, int *tiles_per_image) {
   *tiles_per_image = ((PH + PTH - 1) / PTH) * *tiles_x;
 }
 
+
+size_t ticket_bytes(int N) {
+  return ((size_t)N * sizeof(unsigned) + kTicketAlign - 1) / kTicketAlign * kTicketAlign;
+}
+
+// C_in * C_out * 9 floats; a multiple of 256 bytes for every supported shape
+// (C_in % 8 == 0, C_out % 16 == 0), so the partials stay 256-byte aligned.
+size_t wprep_bytes(int C_in, int C_out) { return (size_t)C_in * C_out * 9 * sizeof(float); }
+
+template <class OC>
+int launch_for(ConvTArgs a, const float *w, float *wprep, long long grid, hipStream_t stream) {
+  const int total = a.C_in * OC::CO * 9;
+  hipLaunchKernelGGL(convT_prepare_weight_kernel<OC>, dim3((total + THREADS - 1) / THREADS),
+                     dim3(THREADS), 0, stream, w, wprep, total);
+  if (launch_status() != CCE_OK) return CCE_ERR_LAUNCH;
+  const bool vec = (a.W % 4 == 0) && ((uintptr_t)a.x % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL((convT2d_pool_htanh_mean_tanh_kernel<OC, true>), dim3((unsigned)grid),
+                       dim3(THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((convT2d_pool_htanh_mean_tanh_kernel<OC, false>), dim3((unsigned)grid),
+                       dim3(THREADS), 0, stream, a);
+  return launch_status();
+}
+
 }  // namespace
 
+bool convT_layer_supported(int C_in, int C_out) {
+  return C_in >= CC && C_in <= 512 && C_in % CC == 0 && (C_out == 16 || C_out == 32 || C_out == 64);
+}
+
 // Workspace: [per-image counters, padded to 256 B][prepared weight][partials].
-size_t convT_workspace_bytes(int N, int H, int W) {
+size_t convT_workspace_bytes(int N, int C_in, int H, int W, int C_out) {
   int tx, tpi;
   convT_tiles(H, W, &tx, &tpi);
-  const size_t tick = ((size_t)N * sizeof(unsigned) + kTicketAlign - 1) / kTicketAlign * kTicketAlign;
-  return tick + kWprepBytes + (size_t)N * tpi * 64 * sizeof(float);
+  return ticket_bytes(N) + wprep_bytes(C_in, C_out) + (size_t)N * tpi * C_out * sizeof(float);
 }
 
 int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b, float *y,
-                                        int N, int H, int W, float lo, float hi, void *workspace,
-                                        hipStream_t stream) {
+                                        int N, int C_in, int H, int W, int C_out, float lo, float hi,
+                                        void *workspace, hipStream_t stream) {
+  if (!convT_layer_supported(C_in, C_out)) return CCE_ERR_UNSUPPORTED;
   ConvTArgs a;
   a.x = x;
   a.w = w;
   a.b = b;
   a.y = y;
+  a.C_in = C_in;
+  a.nchunk = C_in / CC;
   a.H = H;
   a.W = W;
   a.PH = H / 2;  // conv output is H x W at stride 1, padding 1; floor pooling
@@ -329,25 +377,18 @@ int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const fl
   a.lo = lo;
   a.hi = hi;
   a.inv_count = (float)(1.0 / ((double)a.PH * (double)a.PW));
-  const size_t tick = ((size_t)N * sizeof(unsigned) + kTicketAlign - 1) / kTicketAlign * kTicketAlign;
   char *wsp = reinterpret_cast<char *>(workspace);
-  float *wprep = reinterpret_cast<float *>(wsp + tick);
+  float *wprep = reinterpret_cast<float *>(wsp + ticket_bytes(N));
   a.tickets = reinterpret_cast<unsigned *>(wsp);
   a.wprep = wprep;
-  a.partials = reinterpret_cast<float *>(wsp + tick + kWprepBytes);
+  a.partials = reinterpret_cast<float *>(wsp + ticket_bytes(N) + wprep_bytes(C_in, C_out));
   const long long grid = (long long)N * a.tiles_per_image;
   if (grid >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
-  hipLaunchKernelGGL(convT_prepare_weight_kernel, dim3(NCHUNK * WS_FLOATS / THREADS), dim3(THREADS),
-                     0, stream, w, wprep);
-  if (launch_status() != CCE_OK) return CCE_ERR_LAUNCH;
-  const bool vec = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
-  if (vec)
-    hipLaunchKernelGGL(convT2d_pool_htanh_mean_tanh_kernel<true>, dim3((unsigned)grid), dim3(THREADS),
-                       0, stream, a);
-  else
-    hipLaunchKernelGGL(convT2d_pool_htanh_mean_tanh_kernel<false>, dim3((unsigned)grid),
-                       dim3(THREADS), 0, stream, a);
-  return launch_status();
+  switch (C_out) {
+    case 16: return launch_for<OutCh<16>>(a, w, wprep, grid, stream);
+    case 32: return launch_for<OutCh<32>>(a, w, wprep, grid, stream);
+    default: return launch_for<OutCh<64>>(a, w, wprep, grid, stream);
+  }
 }
 
 }  // namespace cce

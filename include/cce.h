@@ -62,7 +62,8 @@ typedef enum {
 const char *cce_status_string(int status);
 
 /* Library ABI version: 100 * major + minor (1.1: further layer shapes for
- * the convolutions, any pooling window and stride for the pooled tail). */
+ * Conv2d and Conv3d, any pooling window and stride for the pooled tail;
+ * 1.2: further channel counts for the fused ConvTranspose2d). */
 int cce_version(void);
 
 /*
@@ -134,11 +135,12 @@ int conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b, 
  * is allocated.  It holds per-image completion counters and per-tile
  * partial sums; one workspace serves one call at a time.
  *
- * Supported: C_in = C_out = 64, k = 3, stride = 1, pad = 1, pool_k =
- * pool_s = 2, H, W >= 2, htanh_lo <= htanh_hi (finite), N >= 1,
+ * Supported: k = 3, stride = 1, pad = 1, pool_k = pool_s = 2; C_in a
+ * multiple of 8 in [8, 512] and C_out in {16, 32, 64} (the page's layer is
+ * 64 -> 64); H, W >= 2, htanh_lo <= htanh_hi (finite), N >= 1,
  * N*C_in*H*W < 2^31.  Anything else returns CCE_ERR_UNSUPPORTED (or
- * CCE_ERR_SHAPE).  The result is deterministic: partial sums are combined
- * in a fixed order.
+ * CCE_ERR_SHAPE / CCE_ERR_TOO_LARGE).  The result is deterministic: partial
+ * sums are combined in a fixed order.
  */
 int convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b, float *y, int N,
                                  int C_in, int H, int W, int C_out, int k, int stride, int pad,

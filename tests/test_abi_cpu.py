@@ -46,7 +46,7 @@ def test_status_strings(lib):
         s = cce.status_string(st)
         assert s and s != "unknown status"
     assert cce.status_string(12345) == "unknown status"
-    assert lib.cce_version() == 101
+    assert lib.cce_version() == 102
 
 
 def c2(lib, x=FAKE, w=FAKE, b=None, y=FAKE, N=1, C_in=8, H=16, W=16, C_out=64, k=3):
@@ -106,7 +106,10 @@ def test_convT_validation(lib):
     assert ct(lib, stride=2) == EUNSUP
     assert ct(lib, pad=0) == EUNSUP
     assert ct(lib, pk=3) == EUNSUP
-    assert ct(lib, C_in=32) == EUNSUP
+    assert ct(lib, C_in=12) == EUNSUP   # C_in must be a multiple of 8
+    assert ct(lib, C_in=520) == EUNSUP  # and at most 512
+    assert ct(lib, C_out=48) == EUNSUP  # C_out in {16, 32, 64}
+    assert ct(lib, C_out=128) == EUNSUP
     assert ct(lib, lo=2.0, hi=1.0) == EUNSUP
     assert ct(lib, w=FAKE + 2) == EALIGN
     assert ct(lib, ws=None) == EWS
@@ -124,6 +127,12 @@ def test_convT_workspace_size(lib):
     assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(128, 64, 256, 256, 64) == 512 + wprep + 128 * 128 * 256
     assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 64, 2, 2, 64) == 256 + wprep + 256
     assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 64, 16, 16, 64, stride=2) == 0
+    # other layer shapes: C_in x C_out x 9 prepared weights, C_out partials per tile
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(3, 8, 35, 42, 16) == \
+        256 + 8 * 16 * 9 * 4 + 3 * (3 * 2) * 16 * 4
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(300, 128, 64, 64, 32) == \
+        1280 + 128 * 32 * 9 * 4 + 300 * (4 * 2) * 32 * 4
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 24, 16, 16, 48) == 0
 
 
 def test_binding_rejects_cpu_tensors():

@@ -206,6 +206,45 @@ def test_convT_small(cce, N, H, W, bias):
     assert_close(y.cpu().numpy()[:, :, 0, 0], ref, f"convT N={N} {H}x{W}")
 
 
+CONVT_LAYERS = [  # (C_in, C_out, N, H, W): W % 4 == 0 takes the 16-byte load path
+    (8, 16, 2, 35, 42),
+    (16, 64, 2, 34, 36),
+    (32, 32, 3, 20, 44),
+    (64, 16, 2, 33, 30),
+    (128, 64, 1, 40, 40),
+    (24, 32, 2, 18, 26),
+    (64, 32, 1, 16, 32),
+]
+
+
+@pytest.mark.parametrize("C_in,C_out,N,H,W", CONVT_LAYERS)
+def test_convT_other_layer_shapes(cce, C_in, C_out, N, H, W):
+    """Channel counts beyond the page's 64 -> 64: C_in / 8 K chunks, C_out / 16
+    MFMA column blocks, C_out partial sums per tile."""
+    p = make_inputs(CONVT, seed=800 + C_in + C_out, N=N, C_in=C_in, H=H, W=W, C_out=C_out, k=3)
+    y = cce.convT2d_pool_htanh_mean_tanh(dev(p["x"]), dev(p["w"]), dev(p["b"]))
+    torch.cuda.synchronize()
+    assert y.shape == (N, C_out, 1, 1)
+    ref = O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], p["b"])
+    assert_close(y.cpu().numpy()[:, :, 0, 0], ref, f"convT {C_in}->{C_out} N={N} {H}x{W}")
+
+
+def test_convT_workspace_shared_between_layer_shapes(cce):
+    """One zeroed workspace serves calls of different channel counts in turn."""
+    shapes = [(64, 64, 3, 36, 40), (8, 16, 5, 22, 18), (32, 32, 2, 48, 20)]
+    need = max(cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(N, ci, H, W, co) for ci, co, N, H, W in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ins = [make_inputs(CONVT, seed=900 + i, N=N, C_in=ci, H=H, W=W, C_out=co, k=3)
+           for i, (ci, co, N, H, W) in enumerate(shapes)]
+    for rep in range(2):
+        for (ci, co, N, H, W), p in zip(shapes, ins):
+            y = cce.convT2d_pool_htanh_mean_tanh(dev(p["x"]), dev(p["w"]), dev(p["b"]), workspace=ws)
+            torch.cuda.synchronize()
+            assert_close(y.cpu().numpy()[:, :, 0, 0], O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], p["b"]),
+                         f"convT shared workspace {ci}->{co} pass {rep}")
+    assert int(ws[:256].count_nonzero()) == 0, "per-image counters not reset"
+
+
 def test_convT_hardtanh_bounds_and_saturation(cce):
     p = make_inputs(CONVT, seed=9, N=2, C_in=64, H=20, W=18, C_out=64, k=3)
     x, w = dev(p["x"]), dev(p["w"])
