@@ -185,8 +185,12 @@ __global__ __launch_bounds__(THREADS) void convT_prepare_weight_kernel(const flo
   wprep[p] = w[((size_t)ci * OC::CO + o) * 9 + (8 - tap)];
 }
 
-template <class OC, bool VEC>
+// NCH > 0: a compile-time chunk count (the page's 64-channel layer, NCH = 8);
+// with the runtime count the compiler schedules the chunk loop's LDS reads
+// later and the kernel runs 5 % slower.
+template <class OC, bool VEC, int NCH>
 __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kernel(ConvTArgs a) {
+  const int nchunk = NCH > 0 ? NCH : a.nchunk;
   constexpr int CO = OC::CO, NT = OC::NT;
   __shared__ __attribute__((aligned(16))) float xs[XS_FLOATS];
   __shared__ __attribute__((aligned(16))) float ws[OC::WS_FLOATS];
@@ -217,9 +221,9 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
   __syncthreads();
 
 #pragma unroll 1
-  for (int c = 0; c < a.nchunk; ++c) {
+  for (int c = 0; c < nchunk; ++c) {
     // Next chunk's global loads are in flight while this chunk's MFMAs run.
-    if (c + 1 < a.nchunk) load_chunk<OC, VEC>(a, n, c + 1, h0, w0, tid, r);
+    if (c + 1 < nchunk) load_chunk<OC, VEC>(a, n, c + 1, h0, w0, tid, r);
 #pragma unroll
     for (int cb = 0; cb < CC / 4; ++cb) {
 #pragma unroll
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
           for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x4(av[mt], bv[nt], acc[mt][nt]);
       }
     }
-    if (c + 1 < a.nchunk) {
+    if (c + 1 < nchunk) {
       __syncthreads();  // every wave is done reading chunk c
       store_chunk(xs, ws, tid, r);
       __syncthreads();
@@ -329,7 +333,7 @@ size_t ticket_bytes(int N) {
 // (C_in % 8 == 0, C_out % 16 == 0), so the partials stay 256-byte aligned.
 size_t wprep_bytes(int C_in, int C_out) { return (size_t)C_in * C_out * 9 * sizeof(float); }
 
-template <class OC>
+template <class OC, int NCH>
 int launch_for(ConvTArgs a, const float *w, float *wprep, long long grid, hipStream_t stream) {
   const int total = a.C_in * OC::CO * 9;
   hipLaunchKernelGGL(convT_prepare_weight_kernel<OC>, dim3((total + THREADS - 1) / THREADS),
@@ -337,10 +341,10 @@ int launch_for(ConvTArgs a, const float *w, float *wprep, long long grid, hipStr
   if (launch_status() != CCE_OK) return CCE_ERR_LAUNCH;
   const bool vec = (a.W % 4 == 0) && ((uintptr_t)a.x % 16 == 0);
   if (vec)
-    hipLaunchKernelGGL((convT2d_pool_htanh_mean_tanh_kernel<OC, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((convT2d_pool_htanh_mean_tanh_kernel<OC, true, NCH>), dim3((unsigned)grid),
                        dim3(THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((convT2d_pool_htanh_mean_tanh_kernel<OC, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((convT2d_pool_htanh_mean_tanh_kernel<OC, false, NCH>), dim3((unsigned)grid),
                        dim3(THREADS), 0, stream, a);
   return launch_status();
 }
@@ -385,9 +389,11 @@ int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const fl
   const long long grid = (long long)N * a.tiles_per_image;
   if (grid >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
   switch (C_out) {
-    case 16: return launch_for<OutCh<16>>(a, w, wprep, grid, stream);
-    case 32: return launch_for<OutCh<32>>(a, w, wprep, grid, stream);
-    default: return launch_for<OutCh<64>>(a, w, wprep, grid, stream);
+    case 16: return launch_for<OutCh<16>, 0>(a, w, wprep, grid, stream);
+    case 32: return launch_for<OutCh<32>, 0>(a, w, wprep, grid, stream);
+    default:
+      if (C_in == 64) return launch_for<OutCh<64>, 64 / CC>(a, w, wprep, grid, stream);
+      return launch_for<OutCh<64>, 0>(a, w, wprep, grid, stream);
   }
 }
 
