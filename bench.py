@@ -162,6 +162,62 @@ def record_traffic(pmc_dir: Path, copy_mib: int, previous: dict | None = None) -
     return out
 
 
+MFMA_COUNTERS = ("MfmaUtil", "MfmaFlopsF32", "SQ_INSTS_VALU_MFMA_F32", "SQ_INSTS_LDS",
+                 "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
+
+
+def record_mfma(pmc_dir: Path, previous: dict | None = None) -> dict:
+    """Turn rocprofv3 runs of `--pmc MfmaUtil MfmaFlopsF32 SQ_INSTS_VALU_MFMA_F32
+    SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE` into per-launch figures of
+    each convolution workload's dominant kernel: the fp32 MFMA FLOPs the
+    hardware counted (against the algorithmic FLOPs) and the matrix cores'
+    busy share of the kernel's active cycles.  Expects <dir>/mfma_<workload>/
+    from `--output-format csv -o run`; keeps records of `previous` whose
+    kernel source digest still matches."""
+    out = {"_about": ("Per-launch rocprofv3 counters of the dominant kernel: MfmaFlopsF32 = "
+                      "512 x SQ_INSTS_VALU_MFMA_MOPS_F32; MfmaUtil = matrix-core busy cycles / "
+                      "(active cycles x SIMDs) in percent; GRBM_GUI_ACTIVE summed over the 8 XCDs; "
+                      "valid while the kernel source digest matches.")}
+    for name, rec in (previous or {}).items():
+        cfg = WORKLOADS.get(name)
+        if cfg and isinstance(rec, dict) and rec.get("source_sha256_16") == source_digest(cfg["op"]):
+            out[name] = rec
+    for name, cfg in WORKLOADS.items():
+        op = cfg["op"]
+        f = pmc_dir / f"mfma_{name}" / "run_counter_collection.csv"
+        if not f.exists() or op in (TAIL_POOL, TAIL_GELU):
+            continue
+        vals = {c: _counter_per_dispatch(f, DOMINANT_KERNEL[op], c) for c in MFMA_COUNTERS}
+        if any(v is None for v in vals.values()):
+            continue
+        alg = work_counts(dict(cfg))["flop"]
+        out[name] = {"kernel": DOMINANT_KERNEL[op], "source_sha256_16": source_digest(op),
+                     "mfma_flops_per_launch": int(vals["MfmaFlopsF32"]), "algorithmic_flops": int(alg),
+                     "mfma_flops_over_algorithmic": round(vals["MfmaFlopsF32"] / alg, 4),
+                     "mfma_util_pct": round(vals["MfmaUtil"], 2),
+                     "mfma_f32_insts": int(vals["SQ_INSTS_VALU_MFMA_F32"]),
+                     "lds_insts": int(vals["SQ_INSTS_LDS"]),
+                     "lds_bank_conflict_cycles": int(vals["SQ_LDS_BANK_CONFLICT"]),
+                     "gui_active_cycles_all_xcds": int(vals["GRBM_GUI_ACTIVE"])}
+    return out
+
+
+def measured_mfma(op: str, workload: str):
+    """The committed MFMA counter record of a workload, while its kernel source
+    still matches the profiled one."""
+    f = ROOT / "profiles" / "mfma_counters.json"
+    if not f.exists():
+        return None
+    try:
+        rec = json.loads(f.read_text()).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_digest(op):
+        return None
+    return {"mfma_util_pct": rec["mfma_util_pct"],
+            "mfma_flops_over_algorithmic": rec["mfma_flops_over_algorithmic"]}
+
+
 def copy_probe(mib: int, reps: int) -> None:
     """A plain device-to-device copy of `mib` MiB, `reps` times: the known-size
     reference that calibrates the HBM byte counters."""
@@ -443,6 +499,9 @@ def main():
     ap.add_argument("--record-traffic", metavar="PMC_DIR",
                     help="only convert rocprofv3 FETCH_SIZE/WRITE_SIZE runs in PMC_DIR into "
                          "profiles/hbm_traffic.json and exit")
+    ap.add_argument("--record-mfma", metavar="PMC_DIR",
+                    help="only convert rocprofv3 MFMA/LDS counter runs in PMC_DIR into "
+                         "profiles/mfma_counters.json and exit")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy")
     ap.add_argument("--unfused", action="store_true",
                     help="also time PyTorch-ROCm's unfused operator sequence per workload (context)")
@@ -454,6 +513,15 @@ def main():
         dest = ROOT / "profiles" / "hbm_traffic.json"
         prev = json.loads(dest.read_text()) if dest.exists() else None
         rec = record_traffic(Path(args.record_traffic), args.copy_mib, prev)
+        dest.parent.mkdir(exist_ok=True)
+        dest.write_text(json.dumps(rec, indent=1) + "\n")
+        print(json.dumps(rec, indent=1))
+        return
+
+    if args.record_mfma:
+        dest = ROOT / "profiles" / "mfma_counters.json"
+        prev = json.loads(dest.read_text()) if dest.exists() else None
+        rec = record_mfma(Path(args.record_mfma), prev)
         dest.parent.mkdir(exist_ok=True)
         dest.write_text(json.dumps(rec, indent=1) + "\n")
         print(json.dumps(rec, indent=1))
@@ -524,6 +592,9 @@ def main():
         # that flushes the L2s and the MALL (the event pair brackets the kernel only)
         "per_call": {k: head[k] for k in ("hot", "cold") if k in head},
     }
+    counters = measured_mfma(shape["op"], args.workload)
+    if counters:  # rocprofv3 cross-check of the dominant kernel (profiles/mfma_counters.json)
+        line["mfma_counters"] = counters
     if args.workload in PAGES_ESTIMATE:
         line["pages_estimate"] = PAGES_ESTIMATE[args.workload]
     if args.unfused:

@@ -27,29 +27,33 @@ __device__ __forceinline__ v4f splat4(float v) { return v4f{v, v, v, v}; }
 // MFMA B-operand order: K-step s covers input channels 4 (s / TAPS) .. + 3 at
 // tap s % TAPS, and
 //   ws[(s * 64 + lane) * NT + nt] = w[16 nt + lane % 16][4 (s / TAPS) + lane / 16][s % TAPS].
-// Consecutive threads read consecutive floats of w (16-byte loads when w is
-// 16-byte aligned), so each wave's load touches two or eight cache lines;
-// the reordering happens on the LDS side.  Needs CI % 4 == 0, CO % 16 == 0.
+// The LDS bank of an element depends only on its output channel o, so
+// consecutive lanes take consecutive output channels (conflict-free writes
+// for C_out = 64) and walk their channel's row of CI * TAPS floats in 16-byte
+// reads when w is 16-byte aligned.  Needs CI % 4 == 0, CO % 16 == 0.
 template <int CI, int CO, int TAPS, int THREADS>
 __device__ __forceinline__ void stage_weights_b(float *ws, const float *__restrict__ w, int tid) {
-  constexpr int NT = CO / 16, TOTAL = CO * CI * TAPS;
+  constexpr int NT = CO / 16, ROW = CI * TAPS;
   static_assert(CI % 4 == 0 && CO % 16 == 0, "whole K-steps and channel blocks");
-  auto place = [&](int e, float v) {
-    const int o = e / (CI * TAPS), r = e - o * (CI * TAPS);
+  auto place = [&](int o, int r, float v) {
     const int ci = r / TAPS, tap = r - ci * TAPS;
     const int s = (ci >> 2) * TAPS + tap, lane = ((ci & 3) << 4) | (o & 15);
     ws[(s * 64 + lane) * NT + (o >> 4)] = v;
   };
   if ((reinterpret_cast<uintptr_t>(w) & 15) == 0) {
-    for (int q = tid; q < TOTAL / 4; q += THREADS) {
-      const v4f v = reinterpret_cast<const v4f *>(w)[q];
-      place(4 * q, v.x);
-      place(4 * q + 1, v.y);
-      place(4 * q + 2, v.z);
-      place(4 * q + 3, v.w);
+    for (int p = tid; p < CO * (ROW / 4); p += THREADS) {  // p = (quad j, channel o)
+      const int o = p % CO, j = p / CO;
+      const v4f v = *reinterpret_cast<const v4f *>(w + o * ROW + 4 * j);
+      place(o, 4 * j, v.x);
+      place(o, 4 * j + 1, v.y);
+      place(o, 4 * j + 2, v.z);
+      place(o, 4 * j + 3, v.w);
     }
   } else {
-    for (int e = tid; e < TOTAL; e += THREADS) place(e, w[e]);
+    for (int p = tid; p < CO * ROW; p += THREADS) {
+      const int o = p % CO, r = p / CO;
+      place(o, r, w[o * ROW + r]);
+    }
   }
 }
 

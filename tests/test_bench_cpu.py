@@ -74,6 +74,27 @@ def test_record_traffic_scales_by_copy_calibration(tmp_path):
     assert rec["conv2d_relu_hswish_n8"]["bytes_per_launch"] == r["bytes_per_launch"]
 
 
+def test_record_mfma_counters(tmp_path):
+    k = "void cce::(anonymous namespace)::convT2d_pool_htanh_mean_tanh_kernel<OutCh<64>, true, 8>(Args)"
+    vals = {"MfmaUtil": 87.5, "MfmaFlopsF32": 4.0e11, "SQ_INSTS_VALU_MFMA_F32": 2.0e8,
+            "SQ_INSTS_LDS": 1.0e7, "SQ_LDS_BANK_CONFLICT": 3.0e5, "GRBM_GUI_ACTIVE": 1.0e7}
+    rows = [{"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v} for c, v in vals.items()]
+    rows += [{"Kernel_Name": k, "Counter_Name": "MfmaUtil", "Counter_Value": 85.5},  # second dispatch
+             {"Kernel_Name": "convT_prepare_weight_kernel", "Counter_Name": "MfmaUtil", "Counter_Value": 0.0}]
+    _write_counter_csv(tmp_path / "mfma_convT2d_pool_htanh_mean_tanh_n16", rows)
+    _write_counter_csv(tmp_path / "mfma_pool_htanh_mean_tanh_n128", rows)  # no MFMA: ignored
+    rec = bench.record_mfma(tmp_path)
+    r = rec["convT2d_pool_htanh_mean_tanh_n16"]
+    alg = bench.work_counts(dict(WORKLOADS["convT2d_pool_htanh_mean_tanh_n16"]))["flop"]
+    assert r["mfma_util_pct"] == 86.5  # mean over the kernel's dispatches only
+    assert r["mfma_flops_per_launch"] == 400_000_000_000 and r["algorithmic_flops"] == alg
+    assert r["mfma_flops_over_algorithmic"] == round(4.0e11 / alg, 4)
+    assert r["source_sha256_16"] == bench.source_digest("convT2d_pool_htanh_mean_tanh")
+    assert "pool_htanh_mean_tanh_n128" not in rec
+    prev = {"conv3d_lrelu_add_clamp_gelu_n128": {"source_sha256_16": "stale", "mfma_util_pct": 1.0}}
+    assert "conv3d_lrelu_add_clamp_gelu_n128" not in bench.record_mfma(tmp_path, prev)
+
+
 def test_bench_refuses_more_than_one_gpu():
     res = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "8"], capture_output=True,
                          text=True, timeout=120)
