@@ -91,6 +91,24 @@ def _dev_ptr(t, name, ndim=None):
     return t.data_ptr()
 
 
+def _dims(t, ndim, name):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def _expect(t, shape, name):
+    """The C ABI takes sizes, not buffers: every tensor handed to it must have
+    exactly the shape the sizes imply, or a kernel would read or write past it."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(x, **ts):
+    for name, t in ts.items():
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} is on {t.device}, x on {x.device}")
+
+
 def _stream(t) -> int:
     import torch
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -103,8 +121,14 @@ def conv2d_relu_hswish(x, w, b=None, out=None):
     """
     import torch
     L = load()
+    _dims(x, 4, "x")
+    _dims(w, 4, "w")
     N, C_in, H, W = x.shape
     C_out, _, k, _ = w.shape
+    _expect(w, (C_out, C_in, k, k), "w")
+    _expect(b, (C_out,), "b")
+    _expect(out, (N, C_out, H - k + 1, W - k + 1), "out")
+    _same_device(x, w=w, b=b, out=out)
     if out is None:
         out = torch.empty((N, C_out, H - k + 1, W - k + 1), device=x.device, dtype=torch.float32)
     st = L.conv2d_relu_hswish(_dev_ptr(x, "x", 4), _dev_ptr(w, "w", 4), _dev_ptr(b, "b", 1),
@@ -122,11 +146,17 @@ def conv3d_lrelu_add_clamp_gelu(x, w, b, s, negative_slope=0.2, clamp_lo=-1.0, c
     """
     import torch
     L = load()
+    _dims(x, 5, "x")
+    _dims(w, 5, "w")
     N, C_in, D, H, W = x.shape
     C_out, _, k, _, _ = w.shape
+    _expect(w, (C_out, C_in, k, k, k), "w")
+    _expect(b, (C_out,), "b")
     if s.numel() != C_out:
         raise ValueError("s must hold one value per output channel")
     s = s.reshape(C_out)
+    _expect(out, (N, C_out, D - k + 1, H - k + 1, W - k + 1), "out")
+    _same_device(x, w=w, b=b, s=s, out=out)
     if out is None:
         out = torch.empty((N, C_out, D - k + 1, H - k + 1, W - k + 1), device=x.device,
                           dtype=torch.float32)
@@ -166,8 +196,14 @@ def convT2d_pool_htanh_mean_tanh(x, w, b=None, stride=1, padding=1, pool_k=2, po
     """
     import torch
     L = load()
+    _dims(x, 4, "x")
+    _dims(w, 4, "w")
     N, C_in, H, W = x.shape
     _, C_out, k, _ = w.shape
+    _expect(w, (C_in, C_out, k, k), "w")
+    _expect(b, (C_out,), "b")
+    _expect(out, (N, C_out, 1, 1), "out")
+    _same_device(x, w=w, b=b, out=out, workspace=workspace)
     if out is None:
         out = torch.empty((N, C_out, 1, 1), device=x.device, dtype=torch.float32)
     need = convT2d_pool_htanh_mean_tanh_workspace_bytes(N, C_in, H, W, C_out, k, stride, padding,
@@ -190,7 +226,10 @@ def pool_htanh_mean_tanh(z, pool_k=2, pool_s=2, htanh_lo=-1.0, htanh_hi=1.0, out
     """tanh(mean_{H,W}(Hardtanh(MaxPool2d(z)))) over a precomputed z [N, C, H, W] -> [N, C, 1, 1]."""
     import torch
     L = load()
+    _dims(z, 4, "z")
     N, C, H, W = z.shape
+    _expect(out, (N, C, 1, 1), "out")
+    _same_device(z, out=out)
     if out is None:
         out = torch.empty((N, C, 1, 1), device=z.device, dtype=torch.float32)
     st = L.pool_htanh_mean_tanh(_dev_ptr(z, "z", 4), _dev_ptr(out, "out", 4), N, C, H, W, pool_k,
@@ -210,6 +249,8 @@ def lrelu_add_clamp_gelu(z, s, negative_slope=0.2, clamp_lo=-1.0, clamp_hi=1.0, 
     if s.numel() != C:
         raise ValueError("s must hold one value per channel")
     s = s.reshape(C)
+    _expect(out, tuple(z.shape), "out")
+    _same_device(z, s=s, out=out)
     if out is None:
         out = torch.empty_like(z)
     st = L.lrelu_add_clamp_gelu(_dev_ptr(z, "z"), _dev_ptr(s, "s", 1), _dev_ptr(out, "out"), N, C, S,

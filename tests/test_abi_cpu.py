@@ -143,6 +143,40 @@ def test_binding_rejects_cpu_tensors():
         cce.conv2d_relu_hswish(x, w, None, out=torch.zeros(1, 64, 6, 6))
 
 
+def test_binding_checks_shapes_before_any_pointer_reaches_the_abi():
+    """The ABI trusts its size arguments, so the binding rejects tensors whose
+    shapes disagree with the sizes it passes (here on CPU tensors: the shape
+    checks come before the device check)."""
+    import torch
+    z = torch.zeros
+    x = z(1, 8, 8, 8)
+    w = z(64, 8, 3, 3)
+    with pytest.raises(ValueError, match="out"):
+        cce.conv2d_relu_hswish(x, w, None, out=z(1, 64, 6, 5))   # too small an output
+    with pytest.raises(ValueError, match="w"):
+        cce.conv2d_relu_hswish(x, z(64, 4, 3, 3))                 # C_in disagrees with x
+    with pytest.raises(ValueError, match="w"):
+        cce.conv2d_relu_hswish(x, z(64, 8, 3, 2))                 # non-square kernel
+    with pytest.raises(ValueError, match="b"):
+        cce.conv2d_relu_hswish(x, w, z(32))
+    with pytest.raises(ValueError, match="x"):
+        cce.conv2d_relu_hswish(z(8, 8, 8), w)
+    x3, w3 = z(1, 8, 5, 6, 6), z(64, 8, 3, 3, 3)
+    with pytest.raises(ValueError, match="out"):
+        cce.conv3d_lrelu_add_clamp_gelu(x3, w3, None, z(64), out=z(1, 64, 3, 4, 3))
+    with pytest.raises(ValueError, match="s"):
+        cce.conv3d_lrelu_add_clamp_gelu(x3, w3, None, z(63))
+    xt = z(1, 64, 8, 8)
+    with pytest.raises(ValueError, match="w"):
+        cce.convT2d_pool_htanh_mean_tanh(xt, z(32, 64, 3, 3))    # [C_out, C_in] order given
+    with pytest.raises(ValueError, match="out"):
+        cce.convT2d_pool_htanh_mean_tanh(xt, z(64, 64, 3, 3), out=z(1, 32, 1, 1))
+    with pytest.raises(ValueError, match="out"):
+        cce.pool_htanh_mean_tanh(z(2, 3, 8, 8), out=z(2, 3))
+    with pytest.raises(ValueError, match="out"):
+        cce.lrelu_add_clamp_gelu(z(2, 3, 4, 4), z(3), out=z(2, 3, 16))
+
+
 def test_tail_validation(lib):
     def pt(z=FAKE, y=FAKE, N=2, C=3, H=8, W=8, pk=2, ps=2, lo=-1.0, hi=1.0):
         return lib.pool_htanh_mean_tanh(z, y, N, C, H, W, pk, ps, lo, hi, None)

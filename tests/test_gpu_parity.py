@@ -395,6 +395,56 @@ def test_elementwise_tail_workload_sampled(cce):
 # HIP graph capture
 # ---------------------------------------------------------------------------
 
+def off(a=None, shape=None):
+    """A GPU tensor (a copy of `a`, or zeros of `shape`) whose data pointer is
+    4 bytes past a 16-byte boundary: 4-byte aligned, as the ABI requires, but
+    not 16-byte aligned, so every kernel takes its scalar load/store paths."""
+    shape = a.shape if a is not None else shape
+    n = int(np.prod(shape))
+    flat = torch.zeros(n + 4, dtype=torch.float32, device="cuda")
+    k = ((4 - flat.data_ptr() % 16) % 16) // 4
+    t = flat[k:k + n].view(shape)
+    if a is not None:
+        t.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+    assert t.data_ptr() % 16 == 4
+    return t
+
+
+@pytest.mark.parametrize("op", [CONV2D, CONV3D, CONVT, TAIL_POOL, TAIL_GELU])
+def test_pointers_not_16_byte_aligned(cce, op):
+    """Every tensor offset by one float from a 16-byte boundary: the weight
+    staging's scalar branch and the scalar load/store instances, at shapes
+    whose sizes would otherwise take the 16-byte paths."""
+    if op == CONV2D:
+        p = make_inputs(CONV2D, seed=61, N=2, C_in=8, H=20, W=24, C_out=64, k=3)
+        y = off(shape=(2, 64, 18, 22))
+        cce.conv2d_relu_hswish(off(p["x"]), off(p["w"]), off(p["b"]), out=y)
+        ref = O.conv2d_relu_hswish(p["x"], p["w"], p["b"])
+    elif op == CONV3D:
+        p = make_inputs(CONV3D, seed=62, N=1, C_in=8, D=5, H=10, W=12, C_out=64, k=3)
+        y = off(shape=(1, 64, 3, 8, 10))
+        cce.conv3d_lrelu_add_clamp_gelu(off(p["x"]), off(p["w"]), off(p["b"]), off(p["s"]), 0.2, -1.0, 1.0,
+                                        out=y)
+        ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"])
+    elif op == CONVT:
+        p = make_inputs(CONVT, seed=63, N=2, C_in=64, H=32, W=36, C_out=64, k=3)
+        y = off(shape=(2, 64, 1, 1))
+        cce.convT2d_pool_htanh_mean_tanh(off(p["x"]), off(p["w"]), off(p["b"]), out=y)
+        ref = O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], p["b"])[:, :, None, None]
+    elif op == TAIL_POOL:
+        p = make_inputs(TAIL_POOL, seed=64, N=2, C=5, H=16, W=24)
+        y = off(shape=(2, 5, 1, 1))
+        cce.pool_htanh_mean_tanh(off(p["z"]), out=y)
+        ref = O.pool_htanh_mean_tanh(p["z"])[:, :, None, None]
+    else:
+        p = make_inputs(TAIL_GELU, seed=65, N=2, C=6, D=3, H=4, W=8)
+        y = off(shape=p["z"].shape)
+        cce.lrelu_add_clamp_gelu(off(p["z"]), off(p["s"]), 0.2, -1.0, 1.0, out=y)
+        ref = O.lrelu_add_clamp_gelu_array(p["z"], p["s"])
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), ref, f"{op} with 4-byte-offset pointers")
+
+
 def test_graph_capture_replays_match_eager(cce):
     """All five operators captured in one HIP graph (torch.cuda.graph) and
     replayed three times, with eager work and a synchronisation between the
