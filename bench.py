@@ -34,7 +34,7 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 from conv_inputs import (CONV2D, CONV3D, CONVT, TAIL_GELU, TAIL_POOL, WORKLOADS,  # noqa: E402
-                         workload_inputs)
+                         make_inputs, workload_inputs)
 
 METRIC = "fused conv+epilogue ms per call, GFLOP/s & % of fp32/HBM roofline (1 MI355X)"
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
@@ -270,6 +270,63 @@ def device_inputs(torch, cce, shape, p):
     return d
 
 
+# Layer shapes beyond the pages' (each parity-tested against the oracle),
+# timed by `--layer-shapes`: (op, sizes).  The first of each group is the
+# page's layer at the same size, for comparison.
+LAYER_SHAPES = (
+    [(CONV2D, dict(N=32, C_in=ci, H=128, W=128, C_out=co, k=k))
+     for ci, co, k in [(8, 64, 3), (4, 16, 1), (16, 64, 1), (8, 32, 3), (16, 32, 3), (16, 64, 3),
+                       (4, 64, 5), (8, 64, 5)]]
+    + [(CONV3D, dict(N=32, C_in=ci, D=16, H=64, W=64, C_out=co, k=3, slope=0.2, lo=-1.0, hi=1.0))
+       for ci, co in [(8, 64), (4, 16), (8, 32), (16, 64)]]
+    + [(CONVT, dict(N=16, C_in=ci, H=256, W=256, C_out=co, k=3, stride=1, pad=1, pool_k=2, pool_s=2,
+                    lo=-1.0, hi=1.0))
+       for ci, co in [(64, 64), (32, 32), (64, 16), (128, 64)]]
+)
+
+
+def time_layer_shapes(torch, cce, steps, warmup, seed, prewarm_s):
+    """Time every entry of LAYER_SHAPES like the main workload (events around
+    `steps` back-to-back calls after `warmup`); the roofline bound is whichever
+    of the fp32 MFMA and HBM times is longer."""
+    rows = []
+    for op, sizes in LAYER_SHAPES:
+        shape = dict(op=op, **sizes)
+        p = make_inputs(op, seed, **{k: v for k, v in sizes.items() if k not in ("slope", "lo", "hi",
+                                                                                 "stride", "pad",
+                                                                                 "pool_k", "pool_s")})
+        d = device_inputs(torch, cce, shape, p)
+        fn = run_op(cce, shape, d)
+        # Generating the inputs leaves the GPU idle; bring its clocks back up.
+        t_end = time.perf_counter() + prewarm_s
+        while time.perf_counter() < t_end:
+            fn()
+            torch.cuda.synchronize()
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(steps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        wc = work_counts(shape)
+        t_mfma = wc["flop"] / (PEAK_FP32_MFMA_TFLOPS * 1e12) * 1e3
+        t_hbm = wc["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
+        rows.append({"op": op, **{k: v for k, v in sizes.items() if k in ("N", "C_in", "C_out", "k", "D", "H", "W")},
+                     "ms_per_call": round(ms, 5), "tflops": round(wc["flop"] / ms / 1e9, 2),
+                     "gbs": round(wc["bytes"] / ms / 1e6, 1),
+                     "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                     "roofline_frac": round(max(t_mfma, t_hbm) / ms, 4)})
+        print(f"# {op} {sizes['C_in']}->{sizes['C_out']} k{sizes['k']} N{sizes['N']}: {ms:.4f} ms, "
+              f"{rows[-1]['bound']} roofline fraction {rows[-1]['roofline_frac']:.3f}", file=sys.stderr, flush=True)
+        del d
+        torch.cuda.empty_cache()
+    return rows
+
+
 # The pages' own back-of-envelope time estimates for the same workloads on
 # other GPUs (none of them measured): context only, never a target.
 PAGES_ESTIMATE = {
@@ -502,6 +559,9 @@ def main():
     ap.add_argument("--record-mfma", metavar="PMC_DIR",
                     help="only convert rocprofv3 MFMA/LDS counter runs in PMC_DIR into "
                          "profiles/mfma_counters.json and exit")
+    ap.add_argument("--layer-shapes", action="store_true",
+                    help="only time the fused operators at the other supported layer shapes and "
+                         "print one JSON line")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy")
     ap.add_argument("--unfused", action="store_true",
                     help="also time PyTorch-ROCm's unfused operator sequence per workload (context)")
@@ -542,6 +602,10 @@ def main():
         return
     import channel_convolution_epilogue_amd as cce
     cce.load()
+    if args.layer_shapes:
+        rows = time_layer_shapes(torch, cce, args.steps, args.warmup, args.seed, args.prewarm)
+        print(json.dumps({"layer_shapes": rows, "steps": args.steps, "warmup": args.warmup}), flush=True)
+        return
 
     shape, head = time_workload(torch, cce, args.workload, args.steps, args.warmup, args.seed,
                                 args.prewarm, args.cold_calls, keep_output=not args.no_cpu_baseline)
