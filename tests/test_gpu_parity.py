@@ -395,6 +395,71 @@ def test_elementwise_tail_workload_sampled(cce):
 # HIP graph capture
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# Sizes at the ABI's limits
+# ---------------------------------------------------------------------------
+
+def gather(y, idx):
+    """y.flatten()[idx] computed on the GPU, returned to the host."""
+    return y.reshape(-1)[torch.from_numpy(idx).cuda()].cpu().numpy()
+
+
+def test_conv2d_output_near_index_limit(cce):
+    """One 5790 x 5788 image: N * C_out * Ho * Wo = 2,143,319,552, within 0.2 %
+    of the 2^31 output limit, on the tuned 16-byte instance (W and the plane
+    are multiples of 4); checked at sampled outputs including the last ones."""
+    p = make_inputs(CONV2D, seed=81, N=1, C_in=8, H=5790, W=5788, C_out=64, k=3)
+    y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
+    torch.cuda.synchronize()
+    total = y.numel()
+    assert total == 64 * 5788 * 5786 and total < 2 ** 31
+    idx = np.unique(np.concatenate([sample_indices(total, 3000, 81), np.arange(total - 300, total),
+                                    63 * 5788 * 5786 + np.arange(200)]))
+    got = gather(y, idx)
+    del y
+    torch.cuda.empty_cache()
+    assert_close(got, O.conv2d_relu_hswish_at(p["x"], p["w"], p["b"], idx), "conv2d near 2^31 outputs")
+
+
+def test_conv3d_output_near_index_limit(cce):
+    """N * C_out * Do * Ho * Wo = 2,111,864,832 (1 x 64 x 128 x 4158 x 62) on the
+    tuned instance for 64-wide rows; sampled outputs including the last ones."""
+    p = make_inputs(CONV3D, seed=82, N=1, C_in=8, D=130, H=4160, W=64, C_out=64, k=3)
+    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, -1.0, 1.0)
+    torch.cuda.synchronize()
+    total = y.numel()
+    assert total == 64 * 128 * 4158 * 62 and total < 2 ** 31
+    idx = np.unique(np.concatenate([sample_indices(total, 3000, 82), np.arange(total - 300, total)]))
+    got = gather(y, idx)
+    del y
+    torch.cuda.empty_cache()
+    assert_close(got, O.conv3d_lrelu_add_clamp_gelu_at(p["x"], p["w"], p["b"], p["s"], idx),
+                 "conv3d near 2^31 outputs")
+
+
+def test_elementwise_tail_plane_longer_than_2_31(cce):
+    """One (n, c) plane of 2^31 + 2^20 + 6 elements (offsets past 32 bits inside
+    a plane), built by tiling a seeded 2^24-element draw on the GPU; the
+    expected value of each sampled element is the oracle's on that element."""
+    C, S = 2, 2 ** 31 + 2 ** 20 + 6
+    small = make_inputs(TAIL_GELU, seed=83, N=1, C=C, D=1, H=1, W=2 ** 23)
+    zs = dev(small["z"]).reshape(-1)
+    z = zs.repeat((C * S + zs.numel() - 1) // zs.numel())[:C * S].reshape(1, C, S)
+    y = cce.lrelu_add_clamp_gelu(z, dev(small["s"]), 0.2, -1.0, 1.0)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([sample_indices(C * S, 4000, 83), np.arange(S - 64, S + 64),
+                                    np.arange(2 ** 31 - 64, 2 ** 31 + 64), np.arange(C * S - 64, C * S)]))
+    zg, got = gather(z, idx), gather(y, idx)
+    del z, y
+    torch.cuda.empty_cache()
+    ch = idx // S
+    ref = np.empty(idx.shape[0])
+    for c in range(C):
+        m = ch == c
+        ref[m] = O.lrelu_add_clamp_gelu_array(zg[m].reshape(1, 1, -1), small["s"][c:c + 1])[0, 0]
+    assert_close(got, ref, "elementwise tail, plane longer than 2^31")
+
+
 def off(a=None, shape=None):
     """A GPU tensor (a copy of `a`, or zeros of `shape`) whose data pointer is
     4 bytes past a 16-byte boundary: 4-byte aligned, as the ABI requires, but
