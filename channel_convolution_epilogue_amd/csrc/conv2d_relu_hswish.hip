@@ -298,10 +298,10 @@ int launch_instance(const Conv2dArgs &a, hipStream_t stream) {
   return launch_status();
 }
 
-// Strip decomposition of one layer shape and its launch.  ALL_PATHS: the
-// shape has instances with 16-byte loads and stores; otherwise only the
-// scalar-load, scalar-store instance exists.
-template <class GEO, bool ALL_PATHS>
+// Strip decomposition of one layer shape and its launch: 16-byte window
+// loads when W % 4 == 0 and x is 16-byte aligned, 16-byte stores when
+// Ho * Wo % 4 == 0 and y is 16-byte aligned, scalar ones otherwise.
+template <class GEO>
 int launch_layer(const float *x, const float *w, const float *b, float *y, int N, int H, int W,
                  hipStream_t stream) {
   Conv2dArgs a;
@@ -315,8 +315,8 @@ int launch_layer(const float *x, const float *w, const float *b, float *y, int N
   a.Wo = W - (GEO::KS - 1);
   a.P = a.Ho * a.Wo;
 
-  const bool vl = ALL_PATHS && (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
-  const bool vs = ALL_PATHS && (a.P % 4 == 0) && ((uintptr_t)y % 16 == 0);
+  const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  const bool vs = (a.P % 4 == 0) && ((uintptr_t)y % 16 == 0);
   // Largest left shift any row's strips take (0 when stores are scalar).
   int sh_max = 0;
   if (vs)
@@ -332,32 +332,30 @@ int launch_layer(const float *x, const float *w, const float *b, float *y, int N
   a.divS = make_fastdiv((uint32_t)a.S);
   a.divG = make_fastdiv((uint32_t)a.G);
 
-  if constexpr (ALL_PATHS) {
-    if (vl) return vs ? launch_instance<GEO, true, true>(a, stream) : launch_instance<GEO, true, false>(a, stream);
-    return vs ? launch_instance<GEO, false, true>(a, stream) : launch_instance<GEO, false, false>(a, stream);
-  } else {
-    return launch_instance<GEO, false, false>(a, stream);
-  }
+  if (vl) return vs ? launch_instance<GEO, true, true>(a, stream) : launch_instance<GEO, true, false>(a, stream);
+  return vs ? launch_instance<GEO, false, true>(a, stream) : launch_instance<GEO, false, false>(a, stream);
 }
 
 }  // namespace
 
 int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
                               int C_in, int H, int W, int C_out, int k, hipStream_t stream) {
-  // The page's layer, 8 -> 64 channels, 3 x 3: strips of 1 row x 16 columns
-  // and every 16-byte path.  Measured on MI355X with 16-wave workgroups (ms):
+  // The page's layer, 8 -> 64 channels, 3 x 3: strips of 1 row x 16 columns.
+  // Measured on MI355X with 16-wave workgroups (ms):
   // 1 x 16: 0.194 at N = 128 and 0.0184 at N = 8 (two rounds per workgroup,
   // so the first round's stores overlap the second round's MFMAs); 2 x 16:
   // 0.196 and 0.0197.  With 8-wave workgroups 2 x 16 was best (0.199), 1 x 32
   // 0.211, 3 x 16 0.294 (spills).
   if (C_in == 8 && C_out == 64 && k == 3)
-    return launch_layer<StripGeo<1, 1, 8, 64, 3>, true>(x, w, b, y, N, H, W, stream);
+    return launch_layer<StripGeo<1, 1, 8, 64, 3>>(x, w, b, y, N, H, W, stream);
   // Other layer shapes whose weights and 16 wave windows fit in LDS: C_in of
   // 4, 8 or 16, C_out of 16, 32 or 64, 1 x 1, 3 x 3 or 5 x 5 kernels (5 x 5
-  // up to 8 input channels); scalar loads and stores.
+  // up to 8 input channels).  The 16-byte paths matter as much here: with
+  // scalar loads the 16-channel and 5 x 5 windows (15-18 floats per lane in
+  // flight) spill, and 16 -> 64, 3 x 3 ran at 0.31 instead of 0.69 of peak.
 #define CCE_CONV2D_LAYER(CI, CO, KS)                                                        \
   if (C_in == CI && C_out == CO && k == KS)                                                \
-    return launch_layer<StripGeo<1, 1, CI, CO, KS>, false>(x, w, b, y, N, H, W, stream);
+    return launch_layer<StripGeo<1, 1, CI, CO, KS>>(x, w, b, y, N, H, W, stream);
 #define CCE_CONV2D_LAYERS_CO(CI, KS) \
   CCE_CONV2D_LAYER(CI, 16, KS) CCE_CONV2D_LAYER(CI, 32, KS) CCE_CONV2D_LAYER(CI, 64, KS)
   CCE_CONV2D_LAYERS_CO(4, 1) CCE_CONV2D_LAYERS_CO(8, 1) CCE_CONV2D_LAYERS_CO(16, 1)

@@ -78,10 +78,11 @@ int cce_version(void);
  * padding 0, the defaults the page's problem uses), r = max(z, 0),
  * y = r * clamp((r + 3) / 6, 0, 1).
  *
- * Supported layers: the page's C_in = 8, C_out = 64, k = 3 (the tuned
- * instance, 16-byte loads and stores), and C_in in {4, 8, 16}, C_out in
- * {16, 32, 64}, k in {1, 3, 5} (k = 5 only for C_in <= 8; scalar loads and
- * stores); any N >= 1 and H, W >= k.  Other layers return
+ * Supported layers: the page's C_in = 8, C_out = 64, k = 3, and C_in in
+ * {4, 8, 16}, C_out in {16, 32, 64}, k in {1, 3, 5} (k = 5 only for
+ * C_in <= 8); any N >= 1 and H, W >= k.  Loads are 16-byte when W % 4 == 0
+ * and x is 16-byte aligned, stores when (H-k+1)*(W-k+1) % 4 == 0 and y is
+ * 16-byte aligned; otherwise 4-byte (same results).  Other layers return
  * CCE_ERR_UNSUPPORTED.  One input image (C_in*H*W floats), one output image
  * and the output pixel count N*(H-k+1)*(W-k+1) must stay below 2^31, else
  * CCE_ERR_TOO_LARGE.
@@ -101,10 +102,10 @@ int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y,
  * LeakyReLU(t) = t for t >= 0, slope * t otherwise; clamp to [lo, hi];
  * GELU(t) = 0.5 t (1 + erf(t / sqrt 2)) (exact, not the tanh form).
  *
- * Supported: k = 3; the page's C_in = 8, C_out = 64 (the tuned instance:
- * 16-byte loads and stores, polynomial GELU when [lo, hi] lies in [-1, 1])
- * and C_in in {4, 8, 16}, C_out in {16, 32, 64} (scalar loads and stores,
- * erff); any N >= 1, D, H, W >= 3 (rows too wide for LDS are split into
+ * Supported: k = 3; C_in in {4, 8, 16}, C_out in {16, 32, 64} (the page's
+ * 8 -> 64 included); 16-byte loads and stores where sizes and alignment
+ * allow; a fitted polynomial for GELU when [lo, hi] lies in [-1, 1], erff
+ * otherwise; any N >= 1, D, H, W >= 3 (rows too wide for LDS are split into
  * column tiles); lo <= hi and all three scalars finite;
  * N*C_out*(D-2)*(H-2)*(W-2) < 2^31.  Anything else returns
  * CCE_ERR_UNSUPPORTED (or CCE_ERR_SHAPE / CCE_ERR_TOO_LARGE).

@@ -82,15 +82,18 @@ def test_conv2d_small(cce, N, H, W, bias):
     assert_close(y.cpu().numpy(), O.conv2d_relu_hswish(p["x"], p["w"], b), f"conv2d N={N} {H}x{W}")
 
 
+@pytest.mark.parametrize("H,W", [(19, 23), (20, 24)])
 @pytest.mark.parametrize("C_in,C_out,k", [(4, 16, 1), (8, 32, 3), (16, 64, 3), (4, 64, 5), (8, 16, 5),
                                          (16, 32, 1), (8, 64, 1), (4, 32, 3)])
-def test_conv2d_other_layer_shapes(cce, C_in, C_out, k):
+def test_conv2d_other_layer_shapes(cce, C_in, C_out, k, H, W):
     """Layer shapes beyond the page's 8 -> 64, 3 x 3 (other channel counts and
-    kernel sizes), on odd sizes that leave ragged strips and row groups."""
-    p = make_inputs(CONV2D, seed=600 + C_in + C_out + k, N=2, C_in=C_in, H=19, W=23, C_out=C_out, k=k)
+    kernel sizes): 19 x 23 takes the scalar loads and stores and leaves ragged
+    strips and row groups; 20 x 24 (W and the output plane multiples of 4)
+    the 16-byte ones."""
+    p = make_inputs(CONV2D, seed=600 + C_in + C_out + k + W, N=2, C_in=C_in, H=H, W=W, C_out=C_out, k=k)
     y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
     torch.cuda.synchronize()
-    assert y.shape == (2, C_out, 19 - k + 1, 23 - k + 1)
+    assert y.shape == (2, C_out, H - k + 1, W - k + 1)
     assert_close(y.cpu().numpy(), O.conv2d_relu_hswish(p["x"], p["w"], p["b"]),
                  f"conv2d {C_in}->{C_out} k={k}")
 
@@ -145,17 +148,19 @@ def test_conv3d_small(cce, N, D, H, W, bias):
     assert_close(y.cpu().numpy(), ref, f"conv3d N={N} {D}x{H}x{W}")
 
 
+@pytest.mark.parametrize("H,W,lo,hi", [(13, 21, -1.0, 1.0), (14, 24, -1.0, 1.0), (14, 24, -2.0, 1.5)])
 @pytest.mark.parametrize("C_in,C_out", [(4, 16), (4, 64), (8, 32), (16, 16), (16, 64)])
-def test_conv3d_other_layer_shapes(cce, C_in, C_out):
-    """Channel counts beyond the page's 8 -> 64 (3 x 3 x 3): scalar paths and
-    erff; 16 -> 64 leaves so little LDS beside its weights that its rows are
-    split into column tiles."""
-    p = make_inputs(CONV3D, seed=700 + C_in + C_out, N=2, C_in=C_in, D=5, H=13, W=21, C_out=C_out, k=3)
-    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, -1.0, 1.0)
+def test_conv3d_other_layer_shapes(cce, C_in, C_out, H, W, lo, hi):
+    """Channel counts beyond the page's 8 -> 64 (3 x 3 x 3).  13 x 21 takes the
+    scalar loads and stores, 14 x 24 the 16-byte ones; clamp bounds inside
+    [-1, 1] the polynomial GELU, wider ones erff.  16 -> 64 leaves so little
+    LDS beside its weights that its rows are split into column tiles."""
+    p = make_inputs(CONV3D, seed=700 + C_in + C_out + W, N=2, C_in=C_in, D=5, H=H, W=W, C_out=C_out, k=3)
+    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, lo, hi)
     torch.cuda.synchronize()
-    assert y.shape == (2, C_out, 3, 11, 19)
-    assert_close(y.cpu().numpy(), O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"]),
-                 f"conv3d {C_in}->{C_out}")
+    assert y.shape == (2, C_out, 3, H - 2, W - 2)
+    assert_close(y.cpu().numpy(), O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"], 0.2, lo, hi),
+                 f"conv3d {C_in}->{C_out} {H}x{W} clamp [{lo}, {hi}]")
 
 
 def test_conv3d_other_epilogue_parameters(cce):
