@@ -298,12 +298,10 @@ size_t ring_floats(int tr, int xc, int *planestride, int *chstride) {
   return (size_t)L::CI * *chstride;
 }
 
-// Tiling of one layer shape and its launch.  ALL_PATHS: the shape has
-// instances with 16-byte loads and stores, compile-time LDS offsets and the
-// polynomial GELU; otherwise the one instance with scalar loads and stores
-// and erff.
-// FIXED64: also the instances with compile-time LDS offsets for 64-wide rows
-// (the page's layer).
+// Tiling of one layer shape and its launch: 16-byte loads and stores where
+// sizes and alignment allow, the polynomial GELU when [lo, hi] lies in
+// [-1, 1].  FIXED64: also the instances with compile-time LDS offsets for
+// 64-wide rows in 8-row tiles (the page's layer).
 template <class L, bool FIXED64>
 int launch_layer(const float *x, const float *w, const float *b, const float *s, float *y, int N,
                  int D, int H, int W, float slope, float lo, float hi, hipStream_t stream) {
