@@ -277,8 +277,8 @@ LAYER_SHAPES = (
     [(CONV2D, dict(N=32, C_in=ci, H=128, W=128, C_out=co, k=k))
      for ci, co, k in [(8, 64, 3), (4, 16, 1), (16, 64, 1), (8, 32, 3), (16, 32, 3), (16, 64, 3),
                        (4, 64, 5), (8, 64, 5)]]
-    + [(CONV3D, dict(N=32, C_in=ci, D=16, H=64, W=64, C_out=co, k=3, slope=0.2, lo=-1.0, hi=1.0))
-       for ci, co in [(8, 64), (4, 16), (8, 32), (16, 64)]]
+    + [(CONV3D, dict(N=32, C_in=ci, D=16, H=64, W=64, C_out=co, k=k, slope=0.2, lo=-1.0, hi=1.0))
+       for ci, co, k in [(8, 64, 3), (4, 16, 3), (8, 32, 3), (16, 64, 3), (8, 64, 1), (16, 64, 1)]]
     + [(CONVT, dict(N=16, C_in=ci, H=256, W=256, C_out=co, k=3, stride=1, pad=1, pool_k=2, pool_s=2,
                     lo=-1.0, hi=1.0))
        for ci, co in [(64, 64), (32, 32), (64, 16), (128, 64)]]

@@ -2,7 +2,8 @@
 
     python -m channel_convolution_epilogue_amd.build [--verbose]
 
-Every source is compiled in one hipcc invocation for --offload-arch=gfx950.
+Each source is compiled by its own hipcc process for --offload-arch=gfx950
+(in parallel, objects under _build/), then the objects are linked.
 Packed fp32 instructions are switched off for the device code
 (-target-feature -packed-fp32-ops); hipcc's host pass warns that it does not
 know that feature, which is harmless.
@@ -13,6 +14,7 @@ import argparse
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -39,27 +41,45 @@ def hipcc() -> str:
     return str(path) if path.exists() else "hipcc"
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
-    tmp = LIB.with_suffix(f".so.tmp{os.getpid()}")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-I", str(INCLUDE), "-I", str(CSRC), "-o", str(tmp)]
-    if verbose:
-        cmd += ["-Rpass-analysis=kernel-resource-usage"]
-    cmd += list(extra or [])
-    # cce_api.cpp is plain HIP host code; compile it as HIP so one driver call links all.
-    for s in SOURCES:
-        src = CSRC / s
-        cmd += (["-x", "hip", str(src), "-x", "none"] if s.endswith(".cpp") else [str(src)])
+NOISE = ("is not a recognized feature for this target", "warnings generated")
+
+
+def _run(cmd: list[str], verbose: bool) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = res.stdout + res.stderr
-    noise = "is not a recognized feature for this target"
-    shown = "\n".join(l for l in out.splitlines() if noise not in l and "warnings generated" not in l)
+    shown = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                      if not any(n in l for n in NOISE))
     if res.returncode != 0:
         sys.stderr.write(shown + "\n")
-        raise RuntimeError(f"hipcc failed (rc={res.returncode})")
-    if verbose and shown.strip():
-        print(shown)
+        raise RuntimeError(f"hipcc failed (rc={res.returncode}): {' '.join(cmd[-3:])}")
+    return shown if verbose else ""
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
+    """Compile every source to an object in parallel (one hipcc per file),
+    then link them into libcce.so."""
+    objdir = PKG / "_build"
+    objdir.mkdir(exist_ok=True)
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-I", str(INCLUDE), "-I", str(CSRC)]
+    if verbose:
+        flags += ["-Rpass-analysis=kernel-resource-usage"]
+    flags += list(extra or [])
+    jobs = []
+    for s in SOURCES:
+        obj = objdir / (Path(s).stem + ".o")
+        # cce_api.cpp is plain HIP host code; compile it as HIP like the kernels.
+        lang = ["-x", "hip"] if s.endswith(".cpp") else []
+        jobs.append((obj, [hipcc(), *flags, "-c", *lang, str(CSRC / s), "-o", str(obj)]))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        outs = list(pool.map(lambda j: _run(j[1], verbose), jobs))
+    tmp = LIB.with_suffix(f".so.tmp{os.getpid()}")
+    outs.append(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp),
+                      *[str(o) for o, _ in jobs]], verbose))
+    for shown in outs:
+        if shown.strip():
+            print(shown)
     os.replace(tmp, LIB)
     return LIB
 

@@ -68,7 +68,7 @@ const char *cce_status_string(int status) {
   }
 }
 
-int cce_version(void) { return 102; }
+int cce_version(void) { return 103; }
 
 // Layer shapes the Conv2d kernel is instantiated for (see the header).
 static bool conv2d_layer_supported(int C_in, int C_out, int k) {
@@ -99,15 +99,17 @@ int conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b, 
   if (!x || !w || !s || !y) return CCE_ERR_NULL;
   if (N < 1 || C_in < 1 || C_out < 1 || k < 1 || D < k || H < k || W < k) return CCE_ERR_SHAPE;
   const bool ci = C_in == 4 || C_in == 8 || C_in == 16, co = C_out == 16 || C_out == 32 || C_out == 64;
-  if (!ci || !co || k != 3) return CCE_ERR_UNSUPPORTED;
+  if (!ci || !co || (k != 3 && k != 1)) return CCE_ERR_UNSUPPORTED;
   if (!is_finite_f(negative_slope) || !is_finite_f(clamp_lo) || !is_finite_f(clamp_hi) || clamp_lo > clamp_hi)
     return CCE_ERR_UNSUPPORTED;
   if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(s) || (b && !aligned4(b)))
     return CCE_ERR_ALIGN;
-  const long long outs = (long long)N * C_out * (D - 2) * (H - 2) * (W - 2);
-  if (outs >= (1LL << 31) || (long long)N * (D - 2) * (H - 2) >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
-  return cce::launch_conv3d_lrelu_add_clamp_gelu(x, w, b, s, y, N, C_in, D, H, W, C_out, negative_slope,
-                                                 clamp_lo, clamp_hi, (hipStream_t)stream);
+  const long long Do = D - k + 1, Ho = H - k + 1, Wo = W - k + 1;
+  const long long outs = (long long)N * C_out * Do * Ho * Wo;
+  if (outs >= (1LL << 31) || (long long)N * Do * Ho >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
+  return cce::launch_conv3d_lrelu_add_clamp_gelu(x, w, b, s, y, N, C_in, D, H, W, C_out, k,
+                                                 negative_slope, clamp_lo, clamp_hi,
+                                                 (hipStream_t)stream);
 }
 
 static int convT_check_shape(int N, int C_in, int H, int W, int C_out, int k, int stride, int pad,

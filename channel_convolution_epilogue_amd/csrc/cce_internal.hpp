@@ -22,10 +22,10 @@ int current_device_info(DeviceInfo *info);  // CCE_OK or CCE_ERR_LAUNCH
 int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
                               int C_in, int H, int W, int C_out, int k, hipStream_t stream);
 
-// Conv3d 3x3x3 (page layer 8 -> 64) + LeakyReLU + add + clamp + GELU.  Validated.
+// Conv3d k^3 (page layer 3^3, 8 -> 64) + LeakyReLU + add + clamp + GELU.  Validated.
 int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,
                                        const float *s, float *y, int N, int C_in, int D, int H,
-                                       int W, int C_out, float slope, float lo, float hi,
+                                       int W, int C_out, int k, float slope, float lo, float hi,
                                        hipStream_t stream);
 
 // ConvTranspose2d 3x3 s1 p1 (C_in % 8 == 0, C_out in {16, 32, 64}) + MaxPool

@@ -1,4 +1,5 @@
-// Conv3d 3x3x3, 8 -> 64 channels, stride 1, padding 0, + bias -> LeakyReLU ->
+// Conv3d k x k x k (the page's 3 x 3 x 3, 8 -> 64 channels; also 1 x 1 x 1 and
+// other channel counts), stride 1, padding 0, + bias -> LeakyReLU ->
 // + s[channel] -> clamp -> exact GELU, fused in one gfx950 kernel
 // (POPCORNBENCH Kimi-K2.6 l2_p90: Conv3d followed by LeakyReLU(0.2), the
 // learnable [C_out,1,1,1] sum_tensor, clamp to [-1, 1] and GELU with
@@ -30,20 +31,20 @@
 namespace cce {
 namespace {
 
-constexpr int KS = 3, TAPS = KS * KS * KS;
 constexpr int WAVES = 16, THREADS = 64 * WAVES;  // one workgroup per CU, 4 waves per SIMD
 
 // Layer shape: CI input channels (a multiple of 4: one per lane group per
-// K-step), CO output channels (16 per MFMA block, at most 64).
-template <int CI_, int CO_>
+// K-step), CO output channels (16 per MFMA block, at most 64), KS x KS x KS
+// kernel.  The LDS ring holds KS + 1 input planes: KS for the current tile
+// and one being filled for the next.
+template <int CI_, int CO_, int KS_>
 struct Layer3 {
-  static constexpr int CI = CI_, CO = CO_;
-  static constexpr int KSTEPS = (CI / 4) * TAPS;      // K-steps of 4 taps (54 for 8 channels)
+  static constexpr int CI = CI_, CO = CO_, KS = KS_, TAPS = KS * KS * KS, SLOTS = KS + 1;
+  static constexpr int KSTEPS = (CI / 4) * TAPS;      // K-steps of 4 taps (54 for 8 channels, 3^3)
   static constexpr int NT = CO / 16;                  // 16-channel MFMA blocks
   static constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // weights, B-operand order (55 KB for 8 -> 64)
   static_assert(CI % 4 == 0 && CO % 16 == 0 && NT >= 1 && NT <= 4, "layer shape");
 };
-constexpr int SLOTS = 4;                     // input planes held in LDS
 constexpr int MT = 2;                        // 16-voxel blocks per wave per pass
 constexpr int kPrefetchPasses = 2;           // a plane of 8 x 10 rows of 64 floats takes 2 passes
 
@@ -60,7 +61,7 @@ struct Conv3dArgs {
   int rowtiles;     // ceil(Ho / TR)
   int coltiles;     // ceil(Wo / TC)
   int nblocks;      // N * rowtiles * coltiles row-column blocks
-  int chstride;     // floats between channels in LDS (SLOTS planes + padding)
+  int chstride;     // floats between channels in LDS (KS + 1 planes + padding)
   int planestride;  // floats between ring slots, (TR + 2) * XC
   float slope, lo, hi;
   FastDiv divRowCol, divCol, divTC, divTClast;
@@ -87,12 +88,14 @@ struct PlaneDst {
 };
 
 // LDS floats for tiles of tr rows whose staged rows hold xc floats: ring
-// slots of (tr + 2) xc floats, channels 16 mod 64 floats apart so the four
-// lane groups of an A read (four channels) start on four different quarters
-// of the 64 LDS banks.
+// slots of (tr + KS - 1) xc floats, channels 16 mod 64 floats apart so the
+// four lane groups of an A read (four channels) start on four different
+// quarters of the 64 LDS banks.
+template <int KS>
 constexpr int plane_floats(int tr, int xc) { return (tr + KS - 1) * xc; }
+template <int KS>
 constexpr int chan_floats(int tr, int xc) {
-  return SLOTS * plane_floats(tr, xc) + ((16 - (SLOTS * plane_floats(tr, xc)) % 64) + 64) % 64;
+  return (KS + 1) * plane_floats<KS>(tr, xc) + ((16 - ((KS + 1) * plane_floats<KS>(tr, xc)) % 64) + 64) % 64;
 }
 
 // FIXED_XC / FIXED_TR: staged row length and tile rows known at compile time
@@ -103,17 +106,18 @@ constexpr int chan_floats(int tr, int xc) {
 template <class L, int FIXED_XC, int FIXED_TR, bool VLOAD, bool VSTORE, bool SERIES>
 __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel(Conv3dArgs a) {
   constexpr int CI = L::CI, CO = L::CO, KSTEPS = L::KSTEPS, NT = L::NT, WS_FLOATS = L::WS_FLOATS;
+  constexpr int KS = L::KS, TAPS = L::TAPS, SLOTS = L::SLOTS;
   const int XC = FIXED_XC ? FIXED_XC : a.XC;
   const int TR = FIXED_TR ? FIXED_TR : a.TR;
-  const int chstride = FIXED_XC ? chan_floats(FIXED_TR, FIXED_XC) : a.chstride;
-  const int planestride = FIXED_XC ? plane_floats(FIXED_TR, FIXED_XC) : a.planestride;
+  const int chstride = FIXED_XC ? chan_floats<KS>(FIXED_TR, FIXED_XC) : a.chstride;
+  const int planestride = FIXED_XC ? plane_floats<KS>(FIXED_TR, FIXED_XC) : a.planestride;
   extern __shared__ __attribute__((aligned(16))) float lds[];
   float *ws = lds;              // weights, B-operand order
   float *xs = lds + WS_FLOATS;  // ring of input planes
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
 
-  // ws[s][lane][nt] = w[16 nt + lane % 16][4 (s / 27) + lane / 16][tap s % 27].
+  // ws[s][lane][nt] = w[16 nt + lane % 16][4 (s / TAPS) + lane / 16][tap s % TAPS].
   stage_weights_b<CI, CO, TAPS, THREADS>(ws, a.w, tid);
   // Bias and the added per-channel term, read from LDS when needed (fewer
   // live registers): ep[c] = b[c], ep[64 + c] = s[c].
@@ -149,8 +153,8 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
     auto src_of = [&](int dd) { return PlaneSrc<CI>{a.x, a.D, a.H, a.W, n, dd, h0, c0}; };
     auto dst_of = [&](int dd) { return PlaneDst<CI>{xs, chstride, (dd % SLOTS) * planestride, XC}; };
 
-    // Planes 0, 1, 2 of this block (every wave is past the previous block's
-    // last barrier, so all slots are free).
+    // Planes 0 .. KS - 1 of this block (every wave is past the previous
+    // block's last barrier, so all slots are free).
 #pragma unroll 1
     for (int dd = 0; dd < KS; ++dd) {
       stage.load(nr, src_of(dd));
@@ -160,11 +164,11 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
 
 #pragma unroll 1
     for (int d = 0; d < a.Do; ++d) {
-      const bool more = d + KS < a.D;  // plane d + 3 exists
+      const bool more = d + KS < a.D;  // plane d + KS exists
       if (more) stage.load(nr, src_of(d + KS));  // in flight during this tile's MFMAs
-      const int so0 = (d % SLOTS) * planestride;
-      const int so1 = ((d + 1) % SLOTS) * planestride;
-      const int so2 = ((d + 2) % SLOTS) * planestride;
+      int so[KS];  // ring slot offsets of planes d .. d + KS - 1
+#pragma unroll
+      for (int kd = 0; kd < KS; ++kd) so[kd] = ((d + kd) % SLOTS) * planestride;
       float *ytile = a.y + (size_t)n * CO * vol + (size_t)d * a.Ho * a.Wo;  // uniform
 
 #pragma unroll 1
@@ -182,9 +186,8 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
           const int v = min(16 * (mb + j) + col, V - 1);
           const int hl = fdiv(v, last_col ? a.divTClast : a.divTC), wl = v - hl * cols;
           const int b0 = g * chstride + hl * XC + wl;
-          base[j][0] = b0 + so0;
-          base[j][1] = b0 + so1;
-          base[j][2] = b0 + so2;
+#pragma unroll
+          for (int kd = 0; kd < KS; ++kd) base[j][kd] = b0 + so[kd];
         }
         v4f acc[MT][NT];
 #pragma unroll
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
 
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          const int tt = s % TAPS, kd = tt / 9, kh = (tt / 3) % 3, kw = tt % 3;
+          const int tt = s % TAPS, kd = tt / (KS * KS), kh = (tt / KS) % KS, kw = tt % KS;
           const int off = (s / TAPS) * 4 * chstride + kh * XC + kw;
           float bv[NT];
           load_b<NT>(bv, &ws[(s * 64 + lane) * NT]);
@@ -252,10 +255,10 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
         }
       }
 
-      // Plane d + 3 goes to slot (d + 3) % 4, last read by tile d - 1, which
+      // Plane d + KS goes to slot (d + KS) % (KS + 1), last read by tile d - 1, which
       // every wave finished before the previous barrier.
       if (more) stage.store(nr, src_of(d + KS), dst_of(d + KS));
-      __syncthreads();  // plane d + 3 visible; plane d free
+      __syncthreads();  // plane d + KS visible; plane d free
     }
   }
 }
@@ -293,8 +296,8 @@ int launch_series(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev,
 
 template <class L>
 size_t ring_floats(int tr, int xc, int *planestride, int *chstride) {
-  *planestride = plane_floats(tr, xc);
-  *chstride = chan_floats(tr, xc);
+  *planestride = plane_floats<L::KS>(tr, xc);
+  *chstride = chan_floats<L::KS>(tr, xc);
   return (size_t)L::CI * *chstride;
 }
 
@@ -317,9 +320,9 @@ int launch_layer(const float *x, const float *w, const float *b, const float *s,
   a.D = D;
   a.H = H;
   a.W = W;
-  a.Do = D - 2;
-  a.Ho = H - 2;
-  a.Wo = W - 2;
+  a.Do = D - (L::KS - 1);
+  a.Ho = H - (L::KS - 1);
+  a.Wo = W - (L::KS - 1);
   a.slope = slope;
   a.lo = lo;
   a.hi = hi;
@@ -343,9 +346,9 @@ int launch_layer(const float *x, const float *w, const float *b, const float *s,
   }
   if (a.TR == 0) {
     a.TR = 8;
-    // Staged columns: TC + 2 rounded up to a multiple of 4.
+    // Staged columns: TC + KS - 1 rounded up to a multiple of 4.
     for (int tc = (a.Wo - 1) & ~3; tc >= 4; tc -= 4) {
-      const int xc = (tc + 2 + 3) & ~3;
+      const int xc = (tc + L::KS - 1 + 3) & ~3;
       ring = ring_floats<L>(a.TR, xc, &a.planestride, &a.chstride);
       if (EXTRA + ring <= budget) {
         a.TC = tc;
@@ -382,21 +385,25 @@ int launch_layer(const float *x, const float *w, const float *b, const float *s,
 
 int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,
                                        const float *s, float *y, int N, int C_in, int D, int H,
-                                       int W, int C_out, float slope, float lo, float hi,
+                                       int W, int C_out, int k, float slope, float lo, float hi,
                                        hipStream_t stream) {
-  // The page's layer, 8 -> 64 channels, with every fast path.
-  if (C_in == 8 && C_out == 64)
-    return launch_layer<Layer3<8, 64>, true>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
-  // Other layer shapes: C_in of 4, 8 or 16, C_out of 16, 32 or 64 (3 x 3 x 3)
-  // with the 16-byte paths and the polynomial GELU but run-time LDS offsets.
-  // Measured (N = 32, 16 x 64 x 64): 4 -> 16 at 0.52 and 8 -> 32 at 0.70 of
-  // peak, against 0.34 and 0.47 with scalar loads, scalar stores and erff.
-#define CCE_CONV3D_LAYER(CI, CO)                                                             \
-  if (C_in == CI && C_out == CO)                                                            \
-    return launch_layer<Layer3<CI, CO>, false>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
-  CCE_CONV3D_LAYER(4, 16) CCE_CONV3D_LAYER(4, 32) CCE_CONV3D_LAYER(4, 64)
-  CCE_CONV3D_LAYER(8, 16) CCE_CONV3D_LAYER(8, 32)
-  CCE_CONV3D_LAYER(16, 16) CCE_CONV3D_LAYER(16, 32) CCE_CONV3D_LAYER(16, 64)
+  // The page's layer, 8 -> 64 channels, 3 x 3 x 3, with every fast path.
+  if (C_in == 8 && C_out == 64 && k == 3)
+    return launch_layer<Layer3<8, 64, 3>, true>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
+  // Other layer shapes: C_in of 4, 8 or 16, C_out of 16, 32 or 64, 3 x 3 x 3 or
+  // 1 x 1 x 1, with the 16-byte paths and the polynomial GELU but run-time LDS
+  // offsets.  Measured (N = 32, 16 x 64 x 64, 3 x 3 x 3): 4 -> 16 at 0.52 and
+  // 8 -> 32 at 0.70 of peak, against 0.34 and 0.47 with scalar loads, scalar
+  // stores and erff.
+#define CCE_CONV3D_LAYER(CI, CO, KS)                                                         \
+  if (C_in == CI && C_out == CO && k == KS)                                                 \
+    return launch_layer<Layer3<CI, CO, KS>, false>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
+  CCE_CONV3D_LAYER(4, 16, 3) CCE_CONV3D_LAYER(4, 32, 3) CCE_CONV3D_LAYER(4, 64, 3)
+  CCE_CONV3D_LAYER(8, 16, 3) CCE_CONV3D_LAYER(8, 32, 3)
+  CCE_CONV3D_LAYER(16, 16, 3) CCE_CONV3D_LAYER(16, 32, 3) CCE_CONV3D_LAYER(16, 64, 3)
+  CCE_CONV3D_LAYER(4, 16, 1) CCE_CONV3D_LAYER(4, 32, 1) CCE_CONV3D_LAYER(4, 64, 1)
+  CCE_CONV3D_LAYER(8, 16, 1) CCE_CONV3D_LAYER(8, 32, 1) CCE_CONV3D_LAYER(8, 64, 1)
+  CCE_CONV3D_LAYER(16, 16, 1) CCE_CONV3D_LAYER(16, 32, 1) CCE_CONV3D_LAYER(16, 64, 1)
 #undef CCE_CONV3D_LAYER
   return CCE_ERR_UNSUPPORTED;
 }

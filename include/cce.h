@@ -63,7 +63,8 @@ const char *cce_status_string(int status);
 
 /* Library ABI version: 100 * major + minor (1.1: further layer shapes for
  * Conv2d and Conv3d, any pooling window and stride for the pooled tail;
- * 1.2: further channel counts for the fused ConvTranspose2d). */
+ * 1.2: further channel counts for the fused ConvTranspose2d; 1.3: 1 x 1 x 1
+ * Conv3d). */
 int cce_version(void);
 
 /*
@@ -102,12 +103,12 @@ int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y,
  * LeakyReLU(t) = t for t >= 0, slope * t otherwise; clamp to [lo, hi];
  * GELU(t) = 0.5 t (1 + erf(t / sqrt 2)) (exact, not the tanh form).
  *
- * Supported: k = 3; C_in in {4, 8, 16}, C_out in {16, 32, 64} (the page's
- * 8 -> 64 included); 16-byte loads and stores where sizes and alignment
- * allow; a fitted polynomial for GELU when [lo, hi] lies in [-1, 1], erff
- * otherwise; any N >= 1, D, H, W >= 3 (rows too wide for LDS are split into
+ * Supported: k = 3 or 1; C_in in {4, 8, 16}, C_out in {16, 32, 64} (the
+ * page's 3 x 3 x 3, 8 -> 64 included); 16-byte loads and stores where sizes
+ * and alignment allow; a fitted polynomial for GELU when [lo, hi] lies in
+ * [-1, 1], erff otherwise; any N >= 1, D, H, W >= k (rows too wide for LDS are split into
  * column tiles); lo <= hi and all three scalars finite;
- * N*C_out*(D-2)*(H-2)*(W-2) < 2^31.  Anything else returns
+ * N*C_out*(D-k+1)*(H-k+1)*(W-k+1) < 2^31.  Anything else returns
  * CCE_ERR_UNSUPPORTED (or CCE_ERR_SHAPE / CCE_ERR_TOO_LARGE).
  */
 int conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b, const float *s,

@@ -46,7 +46,7 @@ def test_status_strings(lib):
         s = cce.status_string(st)
         assert s and s != "unknown status"
     assert cce.status_string(12345) == "unknown status"
-    assert lib.cce_version() == 102
+    assert lib.cce_version() == 103
 
 
 def c2(lib, x=FAKE, w=FAKE, b=None, y=FAKE, N=1, C_in=8, H=16, W=16, C_out=64, k=3):
@@ -84,7 +84,9 @@ def test_conv3d_validation(lib):
     assert c3(lib, C_in=3) == EUNSUP
     assert c3(lib, C_in=32) == EUNSUP
     assert c3(lib, C_out=48) == EUNSUP
-    assert c3(lib, k=5) == EUNSUP
+    assert c3(lib, k=5) == EUNSUP   # 3 x 3 x 3 and 1 x 1 x 1 only
+    assert c3(lib, k=2) == EUNSUP
+    assert c3(lib, k=1, N=1 << 16, D=64, H=64, W=64) == ETOOBIG  # k = 1 keeps every voxel
     assert c3(lib, lo=1.0, hi=-1.0) == EUNSUP
     assert c3(lib, slope=float("nan")) == EUNSUP
     assert c3(lib, hi=float("inf")) == EUNSUP

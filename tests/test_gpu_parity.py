@@ -163,6 +163,19 @@ def test_conv3d_other_layer_shapes(cce, C_in, C_out, H, W, lo, hi):
                  f"conv3d {C_in}->{C_out} {H}x{W} clamp [{lo}, {hi}]")
 
 
+@pytest.mark.parametrize("H,W,lo,hi", [(5, 21, -1.0, 1.0), (6, 24, -1.0, 1.0), (6, 24, -2.0, 1.5)])
+@pytest.mark.parametrize("C_in,C_out", [(4, 16), (8, 64), (16, 32), (16, 64)])
+def test_conv3d_pointwise_layers(cce, C_in, C_out, H, W, lo, hi):
+    """1 x 1 x 1 kernels (a ring of two planes, one K-step per 4 input
+    channels): scalar and 16-byte paths, polynomial GELU and erff."""
+    p = make_inputs(CONV3D, seed=750 + C_in + C_out + W, N=2, C_in=C_in, D=3, H=H, W=W, C_out=C_out, k=1)
+    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, lo, hi)
+    torch.cuda.synchronize()
+    assert y.shape == (2, C_out, 3, H, W)
+    assert_close(y.cpu().numpy(), O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"], 0.2, lo, hi),
+                 f"conv3d 1x1x1 {C_in}->{C_out} {H}x{W} clamp [{lo}, {hi}]")
+
+
 def test_conv3d_other_epilogue_parameters(cce):
     p = make_inputs(CONV3D, seed=7, N=2, C_in=8, D=5, H=10, W=12, C_out=64, k=3)
     x, w, b, s = (dev(p[k]) for k in "xwbs")

@@ -242,6 +242,7 @@ CONV3D_SHAPES = [  # (N, C_in, D, H, W, C_out, k)
     (1, 1, 3, 3, 3, 1, 3),
     (2, 8, 5, 6, 7, 4, 3),
     (1, 2, 4, 3, 5, 3, 2),
+    (2, 4, 3, 4, 5, 16, 1),
 ]
 
 
@@ -253,6 +254,16 @@ def test_conv3d_matches_im2col_and_torch(shape):
     z = O.conv3d(x, w, b)
     np.testing.assert_allclose(z, im2col_conv3d(x, w, b), rtol=0, atol=1e-12)
     np.testing.assert_allclose(z, F.conv3d(_t64(x), _t64(w), _t64(b)).numpy(), rtol=0, atol=1e-12)
+
+
+def test_conv3d_pointwise_is_a_channel_contraction():
+    """A 1 x 1 x 1 convolution is, at every voxel, the matrix product of the
+    [C_out, C_in] weight with the voxel's channel vector, plus the bias."""
+    rng = np.random.default_rng(31)
+    x, w, b = _rand(rng, 2, 16, 3, 4, 5), _rand(rng, 32, 16, 1, 1, 1), _rand(rng, 32)
+    ref = np.einsum("oi,nidhw->nodhw", w[:, :, 0, 0, 0].astype(np.float64), x.astype(np.float64))
+    ref += b.astype(np.float64)[None, :, None, None, None]
+    np.testing.assert_allclose(O.conv3d(x, w, b), ref, rtol=0, atol=1e-12)
 
 
 def test_conv3d_impulse_and_onehot_weight():
