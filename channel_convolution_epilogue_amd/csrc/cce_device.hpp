@@ -31,30 +31,66 @@ __device__ __forceinline__ v4f splat4(float v) { return v4f{v, v, v, v}; }
 // consecutive lanes take consecutive output channels (conflict-free writes
 // for C_out = 64) and walk their channel's row of CI * TAPS floats in 16-byte
 // reads when w is 16-byte aligned.  Needs CI % 4 == 0, CO % 16 == 0.
+//
+// Two phases, so that a kernel's prologue pays one memory latency, not one
+// per pass: load() issues every global read of the weight into registers
+// (a compile-time number of 16-byte reads per thread), place() writes them
+// to LDS.  A kernel issues its other prologue loads (bias, first input tile)
+// between the two.  A weight that is not 16-byte aligned is copied float by
+// float in place().
 template <int CI, int CO, int TAPS, int THREADS>
-__device__ __forceinline__ void stage_weights_b(float *ws, const float *__restrict__ w, int tid) {
-  constexpr int NT = CO / 16, ROW = CI * TAPS;
+struct WeightStageB {
+  static constexpr int NT = CO / 16, ROW = CI * TAPS, QUADS = CO * (ROW / 4);
+  static constexpr int IT = (QUADS + THREADS - 1) / THREADS;  // 16-byte reads per thread
   static_assert(CI % 4 == 0 && CO % 16 == 0, "whole K-steps and channel blocks");
-  auto place = [&](int o, int r, float v) {
-    const int ci = r / TAPS, tap = r - ci * TAPS;
-    const int s = (ci >> 2) * TAPS + tap, lane = ((ci & 3) << 4) | (o & 15);
-    ws[(s * 64 + lane) * NT + (o >> 4)] = v;
-  };
-  if ((reinterpret_cast<uintptr_t>(w) & 15) == 0) {
-    for (int p = tid; p < CO * (ROW / 4); p += THREADS) {  // p = (quad j, channel o)
-      const int o = p % CO, j = p / CO;
-      const v4f v = *reinterpret_cast<const v4f *>(w + o * ROW + 4 * j);
-      place(o, 4 * j, v.x);
-      place(o, 4 * j + 1, v.y);
-      place(o, 4 * j + 2, v.z);
-      place(o, 4 * j + 3, v.w);
-    }
-  } else {
-    for (int p = tid; p < CO * ROW; p += THREADS) {
-      const int o = p % CO, r = p / CO;
-      place(o, r, w[o * ROW + r]);
+  v4f v[IT];
+  bool vec;
+
+  __device__ __forceinline__ void load(const float *__restrict__ w, int tid) {
+    vec = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+    if (!vec) return;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int p = tid + k * THREADS;  // p = (quad j, channel o)
+      if (p < QUADS) {
+        const int o = p % CO, j = p / CO;
+        v[k] = *reinterpret_cast<const v4f *>(w + o * ROW + 4 * j);
+      }
     }
   }
+
+  __device__ __forceinline__ void place(float *ws, const float *__restrict__ w, int tid) const {
+    auto put = [&](int o, int r, float x) {
+      const int ci = r / TAPS, tap = r - ci * TAPS;
+      const int s = (ci >> 2) * TAPS + tap, lane = ((ci & 3) << 4) | (o & 15);
+      ws[(s * 64 + lane) * NT + (o >> 4)] = x;
+    };
+    if (vec) {
+#pragma unroll
+      for (int k = 0; k < IT; ++k) {
+        const int p = tid + k * THREADS;
+        if (p < QUADS) {
+          const int o = p % CO, j = p / CO;
+          put(o, 4 * j, v[k].x);
+          put(o, 4 * j + 1, v[k].y);
+          put(o, 4 * j + 2, v[k].z);
+          put(o, 4 * j + 3, v[k].w);
+        }
+      }
+    } else {
+      for (int p = tid; p < CO * ROW; p += THREADS) {
+        const int o = p % CO, r = p / CO;
+        put(o, r, w[o * ROW + r]);
+      }
+    }
+  }
+};
+
+template <int CI, int CO, int TAPS, int THREADS>
+__device__ __forceinline__ void stage_weights_b(float *ws, const float *__restrict__ w, int tid) {
+  WeightStageB<CI, CO, TAPS, THREADS> st;
+  st.load(w, tid);
+  st.place(ws, w, tid);
 }
 
 // A lane's MFMA B operands of one K-step for NT 16-column channel blocks,

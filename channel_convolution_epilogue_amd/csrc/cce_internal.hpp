@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <atomic>
+
 #include "cce.h"
 
 namespace cce {
@@ -41,6 +43,41 @@ int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, i
                                 int pool_s, float lo, float hi, hipStream_t stream);
 int launch_lrelu_add_clamp_gelu(const float *z, const float *s, float *y, int N, int C, long long S,
                                 float slope, float lo, float hi, hipStream_t stream);
+
+// Launch set-up of one kernel instance: its dynamic-LDS limit raised to the
+// launch's LDS size and its workgroups per CU, done on the first launch on a
+// device and redone only when the LDS size changes (the two runtime calls
+// cost microseconds of host time, which small launches would otherwise pay on
+// every call).  One cache per kernel instance; the entry packs the LDS size
+// and the workgroups per CU into one atomic word, so concurrent callers at
+// worst repeat the set-up.
+constexpr int kLaunchCacheDevices = 64;
+struct LaunchCache {
+  std::atomic<long long> entry[kLaunchCacheDevices];  // (lds_bytes << 8) | per_cu, 0 = unset
+};
+
+// Workgroups of `threads` threads and `lds_bytes` of dynamic LDS that fit on
+// one CU (at least 1), or -1 when the runtime refuses the set-up.
+inline int launch_setup(const void *kern, LaunchCache &cache, int device, size_t lds_bytes,
+                        int threads) {
+  const bool cached = device >= 0 && device < kLaunchCacheDevices;
+  if (cached) {
+    const long long e = cache.entry[device].load(std::memory_order_relaxed);
+    if (e != 0 && (e >> 8) == (long long)lds_bytes) return (int)(e & 255);
+  }
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+      hipSuccess)
+    return -1;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds_bytes) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (per_cu > 255) per_cu = 255;
+  if (cached)
+    cache.entry[device].store(((long long)lds_bytes << 8) | per_cu, std::memory_order_relaxed);
+  return per_cu;
+}
 
 // Map the runtime's last error after a launch onto a cce_status.
 inline int launch_status() {

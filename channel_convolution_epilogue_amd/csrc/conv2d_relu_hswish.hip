@@ -121,8 +121,10 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   // Rounds are workgroup-uniform: round k gives wave w strip
   // wg * WAVES + k * step + w, and a wave whose strip is past the end idles
   // through the round, so every wave meets the same barriers.
+  // A surplus workgroup (the grid is rounded up to a multiple of 8) leaves
+  // after the prologue's loads, so that no branch splits the kernel-argument
+  // reads in two.
   int first = wg * WAVES;
-  if (first >= a.items) return;
   int item = __builtin_amdgcn_readfirstlane(first + wave);
   bool valid = item < a.items;
   if (!valid) item = a.items - 1;
@@ -176,16 +178,19 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
     }
   };
 
-  // The first window's loads go out before the weight staging, so the two
-  // latencies overlap.
+  // Prologue: the first window, the weight and the bias are all requested
+  // before any of them is waited for, so the workgroup waits for one memory
+  // latency before its first MFMA, not one per staging pass.
   Strip cur = decode(item);
   load(cur);
-
   // B operand of K-step s = (channel quad, kh, kw) for all NT 16-channel blocks.
-  stage_weights_b<CI, CO, TAPS, THREADS>(ws, a.w, tid);
+  WeightStageB<CI, CO, TAPS, THREADS> wstage;
+  wstage.load(a.w, tid);
   float bias[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
+  if (first >= a.items) return;  // workgroup-uniform
+  wstage.place(ws, a.w, tid);
   put();
   __syncthreads();  // weights in place; from here on only the per-round barrier
 
@@ -283,13 +288,9 @@ int launch_instance(const Conv2dArgs &a, hipStream_t stream) {
   const size_t lds_bytes = ((size_t)GEO::WS_FLOATS + (size_t)WAVES * GEO::WIN) * sizeof(float);
   if (lds_bytes > dev.lds_per_block) return CCE_ERR_UNSUPPORTED;
   auto kern = conv2d_relu_hswish_kernel<GEO, VL, VS>;
-  if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds_bytes) != hipSuccess)
-    return CCE_ERR_LAUNCH;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, THREADS, lds_bytes) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
+  static LaunchCache cache;
+  const int per_cu = launch_setup((const void *)kern, cache, dev.device, lds_bytes, THREADS);
+  if (per_cu < 0) return CCE_ERR_LAUNCH;
   int grid = dev.num_cus * per_cu;
   const int needed = (a.items + WAVES - 1) / WAVES;
   if (grid > needed) grid = needed;

@@ -278,13 +278,9 @@ template <class L, int FXC, int FTR, bool VL, bool VS, bool SER>
 int launch_instance(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev,
                     hipStream_t stream) {
   auto kern = conv3d_lrelu_add_clamp_gelu_kernel<L, FXC, FTR, VL, VS, SER>;
-  if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds_bytes) != hipSuccess)
-    return CCE_ERR_LAUNCH;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, THREADS, lds_bytes) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
+  static LaunchCache cache;
+  const int per_cu = launch_setup((const void *)kern, cache, dev.device, lds_bytes, THREADS);
+  if (per_cu < 0) return CCE_ERR_LAUNCH;
   int grid = dev.num_cus * per_cu;
   if (grid > a.nblocks) grid = a.nblocks;
   grid = (grid + 7) & ~7;  // the XCD remap needs a multiple of 8; surplus workgroups exit
