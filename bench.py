@@ -588,8 +588,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: every box here has one MI355X and the fused "
-              "kernels have no multi-GPU path (DESIGN.md describes how the batch would shard).",
+        print("bench.py measures one GPU only: the fused kernels have no multi-GPU path. Images "
+              "are independent, so a batch would shard by image across GPUs with no exchange.",
               file=sys.stderr)
         sys.exit(2)
 
