@@ -297,6 +297,70 @@ def test_convT_workspace_reuse_across_shapes_and_determinism(cce):
     assert int(ws[:16].sum().item()) == 0
 
 
+def test_conv3d_alternating_tile_sizes(cce):
+    """One kernel instance launched with a different LDS size on each call
+    (rows of 20 and 44 floats give different plane rings), back and forth,
+    with a 64-wide call of another instance in between: every call matches
+    the oracle, so the cached launch set-up follows the LDS size."""
+    shapes = [(4, 12, 20), (4, 12, 44), (3, 10, 64), (4, 12, 20), (4, 12, 44)]
+    ins = {}
+    for i, (D, H, W) in enumerate(shapes):
+        if (D, H, W) not in ins:
+            p = make_inputs(CONV3D, seed=1100 + i, N=2, C_in=8, D=D, H=H, W=W, C_out=64, k=3)
+            ins[(D, H, W)] = (p, O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"]))
+    for D, H, W in shapes:
+        p, ref = ins[(D, H, W)]
+        y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, -1.0, 1.0)
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy(), ref, f"conv3d alternating W={W}")
+
+
+def test_calls_on_two_streams_at_once(cce):
+    """Work enqueued on two streams runs concurrently; each stream's results
+    are bit-identical to the same calls made one after another (none of the
+    kernels reorders its arithmetic from run to run), and those match the
+    oracle.  Each stream's transposed-convolution call uses its own
+    workspace."""
+    p2 = make_inputs(CONV2D, seed=1201, N=3, C_in=8, H=40, W=36, C_out=64, k=3)
+    p3 = make_inputs(CONV3D, seed=1202, N=1, C_in=8, D=6, H=20, W=24, C_out=64, k=3)
+    pt = [make_inputs(CONVT, seed=1203 + i, N=2, C_in=64, H=32, W=34, C_out=64, k=3) for i in range(2)]
+    x2, w2, b2 = dev(p2["x"]), dev(p2["w"]), dev(p2["b"])
+    x3, w3, b3, s3 = dev(p3["x"]), dev(p3["w"]), dev(p3["b"]), dev(p3["s"])
+    xt = [(dev(p["x"]), dev(p["w"]), dev(p["b"])) for p in pt]
+    need = cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(2, 64, 32, 34, 64)
+    wss = [torch.zeros(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+
+    def run_a():
+        return (cce.conv2d_relu_hswish(x2, w2, b2),
+                cce.convT2d_pool_htanh_mean_tanh(*xt[0], workspace=wss[0]))
+
+    def run_b():
+        return (cce.conv3d_lrelu_add_clamp_gelu(x3, w3, b3, s3, 0.2, -1.0, 1.0),
+                cce.convT2d_pool_htanh_mean_tanh(*xt[1], workspace=wss[1]))
+
+    torch.cuda.synchronize()
+    serial = [t.cpu().numpy() for t in run_a() + run_b()]
+    assert_close(serial[0], O.conv2d_relu_hswish(p2["x"], p2["w"], p2["b"]), "two streams: conv2d")
+    assert_close(serial[2], O.conv3d_lrelu_add_clamp_gelu(p3["x"], p3["w"], p3["b"], p3["s"]),
+                 "two streams: conv3d")
+    for i, k in ((1, 0), (3, 1)):
+        assert_close(serial[i][:, :, 0, 0], O.convT2d_pool_htanh_mean_tanh(pt[k]["x"], pt[k]["w"], pt[k]["b"]),
+                     f"two streams: convT {k}")
+
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            a = run_a()
+        with torch.cuda.stream(s2):
+            b = run_b()
+        torch.cuda.synchronize()
+        for got, want, what in zip(a + b, serial, ("conv2d", "convT 0", "conv3d", "convT 1")):
+            assert np.array_equal(got.cpu().numpy(), want), f"two streams, pass {rep}: {what} differs from serial"
+    assert all(int(ws[:256].count_nonzero()) == 0 for ws in wss), "per-image counters not reset"
+
+
 @pytest.mark.parametrize("name,count", [("convT2d_pool_htanh_mean_tanh_n16", 48),
                                         ("convT2d_pool_htanh_mean_tanh_n128", 32)])
 def test_convT_workload_sampled(cce, name, count):
