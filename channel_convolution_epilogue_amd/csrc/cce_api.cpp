@@ -1,7 +1,7 @@
 // extern "C" entry points of libcce: argument validation (host only, before any
 // HIP call), then one kernel launch per call.  No allocation, no
-// synchronisation and no mutable global state beyond a per-device cache of
-// device properties.
+// synchronisation and no mutable global state beyond per-device caches of
+// device properties and of each kernel instance's launch set-up.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

@@ -44,20 +44,23 @@ int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, i
 int launch_lrelu_add_clamp_gelu(const float *z, const float *s, float *y, int N, int C, long long S,
                                 float slope, float lo, float hi, hipStream_t stream);
 
-// Launch set-up of one kernel instance: its dynamic-LDS limit raised to the
-// launch's LDS size and its workgroups per CU, done on the first launch on a
-// device and redone only when the LDS size changes (the two runtime calls
-// cost microseconds of host time, which small launches would otherwise pay on
-// every call).  One cache per kernel instance; the entry packs the LDS size
-// and the workgroups per CU into one atomic word, so concurrent callers at
-// worst repeat the set-up.
+// Launch set-up of one kernel instance, cached per device: its dynamic-LDS
+// limit is raised once to the device's maximum (so that no call ever lowers
+// it under another thread's launch), and its workgroups per CU are queried
+// for the launch's LDS size and re-queried only when that size changes.  The
+// runtime calls cost microseconds of host time, which small launches would
+// otherwise pay on every call.  One cache per kernel instance; each entry
+// packs the LDS size and the workgroups per CU into one atomic word, so
+// concurrent callers at worst repeat a query.
 constexpr int kLaunchCacheDevices = 64;
 struct LaunchCache {
+  std::atomic<int> raised[kLaunchCacheDevices];       // 1 once the LDS limit is raised
   std::atomic<long long> entry[kLaunchCacheDevices];  // (lds_bytes << 8) | per_cu, 0 = unset
 };
 
 // Workgroups of `threads` threads and `lds_bytes` of dynamic LDS that fit on
-// one CU (at least 1), or -1 when the runtime refuses the set-up.
+// one CU of the current device (at least 1), or -1 when the runtime refuses
+// the set-up.
 inline int launch_setup(const void *kern, LaunchCache &cache, int device, size_t lds_bytes,
                         int threads) {
   const bool cached = device >= 0 && device < kLaunchCacheDevices;
@@ -65,9 +68,14 @@ inline int launch_setup(const void *kern, LaunchCache &cache, int device, size_t
     const long long e = cache.entry[device].load(std::memory_order_relaxed);
     if (e != 0 && (e >> 8) == (long long)lds_bytes) return (int)(e & 255);
   }
-  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
-      hipSuccess)
-    return -1;
+  if (!cached || cache.raised[device].load(std::memory_order_acquire) == 0) {
+    DeviceInfo dev;
+    if (current_device_info(&dev) != CCE_OK || lds_bytes > dev.lds_per_block ||
+        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)dev.lds_per_block) != hipSuccess)
+      return -1;
+    if (cached) cache.raised[device].store(1, std::memory_order_release);
+  }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds_bytes) !=
           hipSuccess ||
