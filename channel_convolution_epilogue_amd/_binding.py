@@ -1,6 +1,7 @@
 """ctypes marshalling for libcce.so.  Same names as the C entry points."""
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import threading
 from pathlib import Path
@@ -37,7 +38,14 @@ def library_path() -> Path:
 
 
 def load() -> ctypes.CDLL:
-    """Load libcce.so (raises if it has not been built)."""
+    """Load libcce.so (raises if it has not been built).
+
+    PyTorch's ROCm wheel carries its own HIP runtime under the same soname
+    (libamdhip64.so.7) as the system one libcce.so is linked against, and
+    whichever is loaded first serves the whole process.  torch is imported
+    first, so libcce binds to the runtime that owns the tensors and streams
+    it is handed; loading libcce first put the system runtime under torch
+    and made every libcce launch fail."""
     global _lib
     with _lock:
         if _lib is not None:
@@ -46,6 +54,7 @@ def load() -> ctypes.CDLL:
             raise ImportError(
                 f"{_LIB_PATH} is missing: build it with "
                 "`python -m channel_convolution_epilogue_amd.build`")
+        import torch  # noqa: F401  (before libcce: one HIP runtime per process)
         L = ctypes.CDLL(str(_LIB_PATH))
         vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.cce_status_string.restype = ctypes.c_char_p
@@ -114,6 +123,17 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _on_device(t):
+    """The library launches on the current HIP device (and sizes its grids
+    for it), so each call runs with the input tensor's device current."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError("the input must be a torch tensor on a GPU")
+    if t.device.index is None or t.device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(t.device)
+
+
 def conv2d_relu_hswish(x, w, b=None, out=None):
     """HardSwish(ReLU(conv2d(x, w, b))), stride 1, padding 0.
 
@@ -131,8 +151,9 @@ def conv2d_relu_hswish(x, w, b=None, out=None):
     _same_device(x, w=w, b=b, out=out)
     if out is None:
         out = torch.empty((N, C_out, H - k + 1, W - k + 1), device=x.device, dtype=torch.float32)
-    st = L.conv2d_relu_hswish(_dev_ptr(x, "x", 4), _dev_ptr(w, "w", 4), _dev_ptr(b, "b", 1),
-                              _dev_ptr(out, "out", 4), N, C_in, H, W, C_out, k, _stream(x))
+    with _on_device(x):
+        st = L.conv2d_relu_hswish(_dev_ptr(x, "x", 4), _dev_ptr(w, "w", 4), _dev_ptr(b, "b", 1),
+                                  _dev_ptr(out, "out", 4), N, C_in, H, W, C_out, k, _stream(x))
     _check("conv2d_relu_hswish", st)
     return out
 
@@ -160,10 +181,11 @@ def conv3d_lrelu_add_clamp_gelu(x, w, b, s, negative_slope=0.2, clamp_lo=-1.0, c
     if out is None:
         out = torch.empty((N, C_out, D - k + 1, H - k + 1, W - k + 1), device=x.device,
                           dtype=torch.float32)
-    st = L.conv3d_lrelu_add_clamp_gelu(_dev_ptr(x, "x", 5), _dev_ptr(w, "w", 5), _dev_ptr(b, "b", 1),
-                                       _dev_ptr(s, "s", 1), _dev_ptr(out, "out", 5), N, C_in, D, H,
-                                       W, C_out, k, float(negative_slope), float(clamp_lo),
-                                       float(clamp_hi), _stream(x))
+    with _on_device(x):
+        st = L.conv3d_lrelu_add_clamp_gelu(_dev_ptr(x, "x", 5), _dev_ptr(w, "w", 5), _dev_ptr(b, "b", 1),
+                                           _dev_ptr(s, "s", 1), _dev_ptr(out, "out", 5), N, C_in, D, H,
+                                           W, C_out, k, float(negative_slope), float(clamp_lo),
+                                           float(clamp_hi), _stream(x))
     _check("conv3d_lrelu_add_clamp_gelu", st)
     return out
 
@@ -214,10 +236,11 @@ def convT2d_pool_htanh_mean_tanh(x, w, b=None, stride=1, padding=1, pool_k=2, po
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = L.convT2d_pool_htanh_mean_tanh(_dev_ptr(x, "x", 4), _dev_ptr(w, "w", 4), _dev_ptr(b, "b", 1),
-                                        _dev_ptr(out, "out", 4), N, C_in, H, W, C_out, k, stride,
-                                        padding, pool_k, pool_s, float(htanh_lo), float(htanh_hi),
-                                        workspace.data_ptr(), ws_bytes, stream)
+    with _on_device(x):
+        st = L.convT2d_pool_htanh_mean_tanh(_dev_ptr(x, "x", 4), _dev_ptr(w, "w", 4), _dev_ptr(b, "b", 1),
+                                            _dev_ptr(out, "out", 4), N, C_in, H, W, C_out, k, stride,
+                                            padding, pool_k, pool_s, float(htanh_lo), float(htanh_hi),
+                                            workspace.data_ptr(), ws_bytes, stream)
     _check("convT2d_pool_htanh_mean_tanh", st)
     return out
 
@@ -232,8 +255,9 @@ def pool_htanh_mean_tanh(z, pool_k=2, pool_s=2, htanh_lo=-1.0, htanh_hi=1.0, out
     _same_device(z, out=out)
     if out is None:
         out = torch.empty((N, C, 1, 1), device=z.device, dtype=torch.float32)
-    st = L.pool_htanh_mean_tanh(_dev_ptr(z, "z", 4), _dev_ptr(out, "out", 4), N, C, H, W, pool_k,
-                                pool_s, float(htanh_lo), float(htanh_hi), _stream(z))
+    with _on_device(z):
+        st = L.pool_htanh_mean_tanh(_dev_ptr(z, "z", 4), _dev_ptr(out, "out", 4), N, C, H, W, pool_k,
+                                    pool_s, float(htanh_lo), float(htanh_hi), _stream(z))
     _check("pool_htanh_mean_tanh", st)
     return out
 
@@ -253,7 +277,8 @@ def lrelu_add_clamp_gelu(z, s, negative_slope=0.2, clamp_lo=-1.0, clamp_hi=1.0, 
     _same_device(z, s=s, out=out)
     if out is None:
         out = torch.empty_like(z)
-    st = L.lrelu_add_clamp_gelu(_dev_ptr(z, "z"), _dev_ptr(s, "s", 1), _dev_ptr(out, "out"), N, C, S,
-                                float(negative_slope), float(clamp_lo), float(clamp_hi), _stream(z))
+    with _on_device(z):
+        st = L.lrelu_add_clamp_gelu(_dev_ptr(z, "z"), _dev_ptr(s, "s", 1), _dev_ptr(out, "out"), N, C, S,
+                                    float(negative_slope), float(clamp_lo), float(clamp_hi), _stream(z))
     _check("lrelu_add_clamp_gelu", st)
     return out

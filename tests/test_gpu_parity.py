@@ -635,3 +635,28 @@ def test_graph_capture_replays_match_eager(cce):
         for i, (o, e) in enumerate(zip(outs, eager)):
             assert torch.equal(o, e), f"replay {rep}, operator {i}"
     assert_close(eager[0].cpu().numpy(), O.conv2d_relu_hswish(p2["x"], p2["w"], p2["b"]), "graph conv2d")
+
+
+def test_library_loaded_before_torch_in_a_fresh_process():
+    """Loading libcce before anything imports torch (as a build step that
+    ends by loading the library does) still leaves one HIP runtime in the
+    process: a call then succeeds and matches the oracle."""
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import channel_convolution_epilogue_amd as cce\n"
+        "cce.load()\n"
+        "import numpy as np, torch\n"
+        "import oracle as O\n"
+        "from conv_inputs import CONV2D, make_inputs\n"
+        "p = make_inputs(CONV2D, seed=5, N=2, C_in=8, H=30, W=26, C_out=64, k=3)\n"
+        "t = lambda a: torch.from_numpy(a).cuda()\n"
+        "y = cce.conv2d_relu_hswish(t(p['x']), t(p['w']), t(p['b'])).cpu().numpy()\n"
+        "ref = O.conv2d_relu_hswish(p['x'], p['w'], p['b'])\n"
+        "assert np.all(np.abs(y - ref) <= 1e-4 + 1e-4 * np.abs(ref))\n"
+        "print('ok', flush=True)\n" % str(root))
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=110)
+    assert res.returncode == 0 and "ok" in res.stdout, res.stdout + res.stderr
