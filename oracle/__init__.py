@@ -45,10 +45,14 @@ _c_dbl = ctypes.c_double
 
 
 def lib() -> ctypes.CDLL:
-    """Load liboracle.so, compiling it first if it is missing or stale."""
+    """Load liboracle.so, compiling it first if it is missing or stale.
+
+    CCE_ORACLE_LIB, when set, names another build of oracle.c to load instead
+    (the mutation test points it at copies with a planted mistake)."""
     global _lib
     if _lib is None:
-        path = build(force=False)
+        override = os.environ.get("CCE_ORACLE_LIB")
+        path = Path(override) if override else build(force=False)
         L = ctypes.CDLL(str(path))
         L.oracle_num_threads.restype = _c_int
         L.oracle_set_num_threads.argtypes = [_c_int]
