@@ -110,7 +110,7 @@ DOMINANT_KERNEL = {  # substring of the kernel symbol that dominates each operat
     CONV3D: "conv3d_lrelu_add_clamp_gelu_kernel",
     CONVT: "convT2d_pool_htanh_mean_tanh_kernel",
     TAIL_POOL: "::pool_htanh_mean_tanh_kernel",
-    TAIL_GELU: "::lrelu_add_clamp_gelu_kernel",
+    TAIL_GELU: "::lrelu_add_clamp_gelu_",  # the flat 16-byte kernel or the per-plane one
 }
 COPY_KERNEL = "copyBuffer"  # torch's device-to-device copy under ROCm
 

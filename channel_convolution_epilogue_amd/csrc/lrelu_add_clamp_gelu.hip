@@ -5,20 +5,30 @@
 // (one fused kernel after a library Conv3d); here it is the HBM read+write
 // bound companion of the fully fused operator.
 //
-// Design: a 1-D grid of workgroups, each owning a 4096-element chunk of one
-// (n, c) plane, so the channel offset s[c] is one value per workgroup.  With S
-// a multiple of 4 every thread moves four 16-byte quads (loads issued first);
-// otherwise single floats.  The arithmetic is the same device function the
-// fused Conv3d kernel applies to its accumulators.
+// Design.  With S a multiple of 4 and 16-byte aligned buffers (the usual
+// case) the array is one flat stream of 16-byte quads, no quad straddling
+// two (n, c) planes: one-wave workgroups, one quad per thread, the channel
+// of each quad found by two multiplicative divisions of its index, loads
+// and stores non-temporal (each is touched once).  Consecutive workgroups
+// take consecutive 1 KB runs, so every 128-byte line is written whole by
+// one wave.  Measured on MI355X over [128, 64, 14, 62, 62]: 0.53 ms
+// (6.7 TB/s read + write), against 0.65 ms for 4096-element chunks of one
+// plane per 256-thread workgroup (each plane's last chunk mostly idle, and
+// chunk edges splitting lines between workgroups); four quads per thread,
+// bigger workgroups or cached loads and stores were each slower.
+// Otherwise (S not a multiple of 4, unaligned buffers, or more than 2^31
+// quads) each workgroup takes a chunk of one plane, float by float.  The
+// arithmetic is the same device function the fused Conv3d kernel applies to
+// its accumulators.
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
 
 namespace cce {
 namespace {
 
-constexpr int THREADS = 256;
-constexpr int QPT = 4;                       // quads per thread
-constexpr int CHUNK = THREADS * QPT * 4;     // elements per workgroup
+constexpr int THREADS = 256;                // per-plane path
+constexpr int CHUNK = THREADS * 16;         // elements per workgroup, per-plane path
+constexpr int FLAT_THREADS = 64;            // flat quad path: one wave per workgroup
 
 // z and y may be the same buffer (in place): every element is read and then
 // written by the same thread, so they are not declared __restrict__.
@@ -27,12 +37,29 @@ struct EltArgs {
   const float *__restrict__ s;
   float *y;
   long long S;
-  int C, chunks;  // chunks per plane
-  FastDiv divChunks;
+  int C, chunks;  // chunks per plane (per-plane path)
+  int quads;      // N * C * S / 4 (flat path, below 2^31)
+  FastDiv divChunks, divSq, divC;  // chunks; S / 4; C
   float slope, lo, hi;
 };
 
-template <bool VEC, bool SERIES>
+template <bool SERIES>
+__global__ __launch_bounds__(FLAT_THREADS) void lrelu_add_clamp_gelu_flat_kernel(EltArgs a) {
+  const int q = blockIdx.x * FLAT_THREADS + threadIdx.x;
+  if (q >= a.quads) return;
+  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(a.z) + q);
+  const int plane = fdiv(q, a.divSq);
+  const int c = plane - fdiv(plane, a.divC) * a.C;
+  const float sadd = a.s[c];
+  v4f r;
+  r.x = lrelu_add_clamp_gelu_value<SERIES>(v.x, sadd, a.slope, a.lo, a.hi);
+  r.y = lrelu_add_clamp_gelu_value<SERIES>(v.y, sadd, a.slope, a.lo, a.hi);
+  r.z = lrelu_add_clamp_gelu_value<SERIES>(v.z, sadd, a.slope, a.lo, a.hi);
+  r.w = lrelu_add_clamp_gelu_value<SERIES>(v.w, sadd, a.slope, a.lo, a.hi);
+  __builtin_nontemporal_store(r, reinterpret_cast<v4f *>(a.y) + q);
+}
+
+template <bool SERIES>
 __global__ __launch_bounds__(THREADS) void lrelu_add_clamp_gelu_kernel(EltArgs a) {
   const int plane = fdiv(blockIdx.x, a.divChunks);
   const int chunk = blockIdx.x - plane * a.chunks;
@@ -43,38 +70,8 @@ __global__ __launch_bounds__(THREADS) void lrelu_add_clamp_gelu_kernel(EltArgs a
   const int n_here = left < CHUNK ? (int)left : CHUNK;
   const float *zp = a.z + base;
   float *yp = a.y + base;
-  if (VEC) {
-    // S % 4 == 0: every quad lies in one plane and is 16-byte aligned.
-    v4f v[QPT];
-#pragma unroll
-    for (int k = 0; k < QPT; ++k) {
-      const int e = 4 * (threadIdx.x + k * THREADS);
-      if (e < n_here) v[k] = *reinterpret_cast<const v4f *>(zp + e);
-    }
-#pragma unroll
-    for (int k = 0; k < QPT; ++k) {
-      const int e = 4 * (threadIdx.x + k * THREADS);
-      if (e < n_here) {
-        v4f r = v[k];
-        r.x = lrelu_add_clamp_gelu_value<SERIES>(r.x, sadd, a.slope, a.lo, a.hi);
-        r.y = lrelu_add_clamp_gelu_value<SERIES>(r.y, sadd, a.slope, a.lo, a.hi);
-        r.z = lrelu_add_clamp_gelu_value<SERIES>(r.z, sadd, a.slope, a.lo, a.hi);
-        r.w = lrelu_add_clamp_gelu_value<SERIES>(r.w, sadd, a.slope, a.lo, a.hi);
-        store4(yp + e, r);
-      }
-    }
-  } else {
-    for (int e = threadIdx.x; e < n_here; e += THREADS)
-      yp[e] = lrelu_add_clamp_gelu_value<SERIES>(zp[e], sadd, a.slope, a.lo, a.hi);
-  }
-}
-
-template <bool VEC>
-void launch_vec(const EltArgs &a, unsigned grid, hipStream_t stream) {
-  if (a.lo >= -1.0f && a.hi <= 1.0f)
-    hipLaunchKernelGGL((lrelu_add_clamp_gelu_kernel<VEC, true>), dim3(grid), dim3(THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL((lrelu_add_clamp_gelu_kernel<VEC, false>), dim3(grid), dim3(THREADS), 0, stream, a);
+  for (int e = threadIdx.x; e < n_here; e += THREADS)
+    yp[e] = lrelu_add_clamp_gelu_value<SERIES>(zp[e], sadd, a.slope, a.lo, a.hi);
 }
 
 }  // namespace
@@ -87,19 +84,33 @@ int launch_lrelu_add_clamp_gelu(const float *z, const float *s, float *y, int N,
   a.y = y;
   a.S = S;
   a.C = C;
+  a.slope = slope;
+  a.lo = lo;
+  a.hi = hi;
+  const bool series = lo >= -1.0f && hi <= 1.0f;
+  const long long quads = (long long)N * C * (S / 4);
+  const bool flat = (S % 4 == 0) && ((uintptr_t)z % 16 == 0) && ((uintptr_t)y % 16 == 0) &&
+                    quads < (1LL << 31);
+  if (flat) {
+    a.quads = (int)quads;
+    a.divSq = make_fastdiv((uint32_t)(S / 4));
+    a.divC = make_fastdiv((uint32_t)C);
+    const unsigned grid = (unsigned)((quads + FLAT_THREADS - 1) / FLAT_THREADS);
+    if (series)
+      hipLaunchKernelGGL(lrelu_add_clamp_gelu_flat_kernel<true>, dim3(grid), dim3(FLAT_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL(lrelu_add_clamp_gelu_flat_kernel<false>, dim3(grid), dim3(FLAT_THREADS), 0, stream, a);
+    return launch_status();
+  }
   const long long chunks = (S + CHUNK - 1) / CHUNK;
   const long long grid = (long long)N * C * chunks;
   if (grid >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
   a.chunks = (int)chunks;
   a.divChunks = make_fastdiv((uint32_t)chunks);
-  a.slope = slope;
-  a.lo = lo;
-  a.hi = hi;
-  const bool vec = (S % 4 == 0) && ((uintptr_t)z % 16 == 0) && ((uintptr_t)y % 16 == 0);
-  if (vec)
-    launch_vec<true>(a, (unsigned)grid, stream);
+  if (series)
+    hipLaunchKernelGGL(lrelu_add_clamp_gelu_kernel<true>, dim3((unsigned)grid), dim3(THREADS), 0, stream, a);
   else
-    launch_vec<false>(a, (unsigned)grid, stream);
+    hipLaunchKernelGGL(lrelu_add_clamp_gelu_kernel<false>, dim3((unsigned)grid), dim3(THREADS), 0, stream, a);
   return launch_status();
 }
 

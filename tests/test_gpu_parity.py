@@ -414,7 +414,10 @@ def test_pool_tail_workload_full(cce):
 
 
 @pytest.mark.parametrize("N,C,D,H,W", [(2, 64, 3, 10, 12), (1, 3, 1, 1, 7), (3, 5, 2, 9, 11),
-                                       (1, 64, 14, 62, 62)])
+                                       (1, 64, 14, 62, 62),
+                                       (3, 5, 1, 1, 4),    # one quad per plane, odd channel count
+                                       (2, 1, 1, 2, 8),    # one channel
+                                       (5, 7, 2, 3, 12)])  # ragged last one-wave workgroup
 def test_elementwise_tail_small(cce, N, C, D, H, W):
     p = make_inputs(TAIL_GELU, seed=500 + N * C, N=N, C=C, D=D, H=H, W=W)
     s = p["s"] * 20
