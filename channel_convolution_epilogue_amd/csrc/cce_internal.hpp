@@ -24,6 +24,13 @@ int current_device_info(DeviceInfo *info);  // CCE_OK or CCE_ERR_LAUNCH
 int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y, int N,
                               int C_in, int H, int W, int C_out, int k, hipStream_t stream);
 
+// 1 x 1 Conv2d over `rows` x W pixels + LeakyReLU + add + clamp + GELU: the
+// 1 x 1 x 1 Conv3d layers (rows = D * H), on the Conv2d strip kernel.
+int launch_pointwise_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,
+                                          const float *s, float *y, int N, int C_in, int rows,
+                                          int W, int C_out, float slope, float lo, float hi,
+                                          hipStream_t stream);
+
 // Conv3d k^3 (page layer 3^3, 8 -> 64) + LeakyReLU + add + clamp + GELU.  Validated.
 int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b,
                                        const float *s, float *y, int N, int C_in, int D, int H,

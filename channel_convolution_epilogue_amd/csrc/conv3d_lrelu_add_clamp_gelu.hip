@@ -1,5 +1,6 @@
-// Conv3d k x k x k (the page's 3 x 3 x 3, 8 -> 64 channels; also 1 x 1 x 1 and
-// other channel counts), stride 1, padding 0, + bias -> LeakyReLU ->
+// Conv3d k x k x k (the page's 3 x 3 x 3, 8 -> 64 channels, and other channel
+// counts; 1 x 1 x 1 layers run on the Conv2d strip kernel, see the dispatch at
+// the end), stride 1, padding 0, + bias -> LeakyReLU ->
 // + s[channel] -> clamp -> exact GELU, fused in one gfx950 kernel
 // (POPCORNBENCH Kimi-K2.6 l2_p90: Conv3d followed by LeakyReLU(0.2), the
 // learnable [C_out,1,1,1] sum_tensor, clamp to [-1, 1] and GELU with
@@ -399,20 +400,23 @@ int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const flo
   // The page's layer, 8 -> 64 channels, 3 x 3 x 3, with every fast path.
   if (C_in == 8 && C_out == 64 && k == 3)
     return launch_layer<Layer3<8, 64, 3>, true>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
-  // Other layer shapes: C_in of 4, 8 or 16, C_out of 16, 32 or 64, 3 x 3 x 3 or
-  // 1 x 1 x 1, with the 16-byte paths and the polynomial GELU but run-time LDS
-  // offsets.  Measured (N = 32, 16 x 64 x 64, 3 x 3 x 3): 4 -> 16 at 0.52 and
-  // 8 -> 32 at 0.70 of peak, against 0.34 and 0.47 with scalar loads, scalar
-  // stores and erff.
+  // A 1 x 1 x 1 layer is a 1 x 1 Conv2d over D * H rows of W pixels: it runs
+  // on the Conv2d strip kernel with this operator's epilogue.  (On this
+  // kernel its two K-steps per tile left the plane staging and the per-tile
+  // barrier exposed: 0.17 ms for 8 -> 64 at N = 32, 16 x 64 x 64.)
+  if (k == 1)
+    return launch_pointwise_lrelu_add_clamp_gelu(x, w, b, s, y, N, C_in, D * H, W, C_out, slope,
+                                                 lo, hi, stream);
+  // Other 3 x 3 x 3 layer shapes: C_in of 4, 8 or 16, C_out of 16, 32 or 64,
+  // with the 16-byte paths and the polynomial GELU but run-time LDS offsets.
+  // Measured (N = 32, 16 x 64 x 64): 4 -> 16 at 0.52 and 8 -> 32 at 0.70 of
+  // peak, against 0.34 and 0.47 with scalar loads, scalar stores and erff.
 #define CCE_CONV3D_LAYER(CI, CO, KS)                                                         \
   if (C_in == CI && C_out == CO && k == KS)                                                 \
     return launch_layer<Layer3<CI, CO, KS>, false>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
   CCE_CONV3D_LAYER(4, 16, 3) CCE_CONV3D_LAYER(4, 32, 3) CCE_CONV3D_LAYER(4, 64, 3)
   CCE_CONV3D_LAYER(8, 16, 3) CCE_CONV3D_LAYER(8, 32, 3)
   CCE_CONV3D_LAYER(16, 16, 3) CCE_CONV3D_LAYER(16, 32, 3) CCE_CONV3D_LAYER(16, 64, 3)
-  CCE_CONV3D_LAYER(4, 16, 1) CCE_CONV3D_LAYER(4, 32, 1) CCE_CONV3D_LAYER(4, 64, 1)
-  CCE_CONV3D_LAYER(8, 16, 1) CCE_CONV3D_LAYER(8, 32, 1) CCE_CONV3D_LAYER(8, 64, 1)
-  CCE_CONV3D_LAYER(16, 16, 1) CCE_CONV3D_LAYER(16, 32, 1) CCE_CONV3D_LAYER(16, 64, 1)
 #undef CCE_CONV3D_LAYER
   return CCE_ERR_UNSUPPORTED;
 }
