@@ -6,7 +6,7 @@ HardSwish constant, LeakyReLU sign, GELU scale, epilogue order, pooling
 window, output size or mean divisor), compiles it with gcc, and runs the pin
 suite (tests/test_oracle_pins.py) against that library in a fresh process:
 the suite must fail.  A control copy with no change must pass, so a failure
-is the mutant's, not the harness's.  CPU only; the planted mistakes live in
+is the mutant's, not the test's own machinery.  CPU only; the planted mistakes live in
 temporary copies and never touch the real oracle.
 """
 import os
@@ -98,7 +98,7 @@ def test_pins_catch_planted_mistake(tmp_path, name):
         text = text.replace(old, new)
     res = _build_and_run_pins(tmp_path, text)
     tail = res.stdout.strip().splitlines()[-1] if res.stdout.strip() else ""
-    # A pin must fail (an assertion), not the harness (collection or import errors).
+    # A pin must fail (an assertion), not the test run itself (collection or import errors).
     assert res.returncode == 1 and " failed" in tail and "error" not in tail, \
         f"{name}: pins did not catch it (rc={res.returncode}): {tail}\n{res.stderr[-2000:]}"
     caught = [l.split(" - ")[0].split("::")[-1] for l in res.stdout.splitlines() if l.startswith("FAILED")]
