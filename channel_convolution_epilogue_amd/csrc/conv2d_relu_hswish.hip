@@ -33,6 +33,9 @@
 //    16-byte read per K-step serves all four 16-channel blocks.
 //  * Bias is the accumulator's initial value; ReLU and HardSwish are applied
 //    in registers before the store: the conv result never reaches memory.
+//  * The same kernel, with the Conv3d operator's epilogue (LeakyReLU, + s[c],
+//    clamp, GELU) as a template parameter, runs the 1 x 1 x 1 Conv3d layers:
+//    a pointwise Conv3d over D x H x W is a 1 x 1 Conv2d over D * H rows.
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
 
