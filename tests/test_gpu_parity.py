@@ -663,3 +663,85 @@ def test_library_loaded_before_torch_in_a_fresh_process():
         "print('ok', flush=True)\n" % str(root))
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=110)
     assert res.returncode == 0 and "ok" in res.stdout, res.stdout + res.stderr
+
+
+# ---------------------------------------------------------------------------
+# Seeded sweep of random shapes: every operator, supported layer shapes,
+# ragged / odd / minimal sizes, 16-byte and scalar paths, both GELU forms.
+# ---------------------------------------------------------------------------
+
+def _sweep_cases(seed, count, draw):
+    rng = np.random.default_rng(seed)
+    return [draw(rng) for _ in range(count)]
+
+
+def test_random_shape_sweep_conv2d(cce):
+    def draw(rng):
+        C_in = int(rng.choice([4, 8, 16]))
+        C_out = int(rng.choice([16, 32, 64]))
+        k = int(rng.choice([1, 3, 5] if C_in <= 8 else [1, 3]))
+        return dict(N=int(rng.integers(1, 4)), C_in=C_in, C_out=C_out, k=k,
+                    H=int(rng.integers(k, 41)), W=int(rng.integers(k, 41)), bias=bool(rng.random() < 0.8))
+    for i, c in enumerate(_sweep_cases(2024, 24, draw)):
+        print(f"sweep conv2d case {i}: {c}", flush=True)
+        p = make_inputs(CONV2D, seed=3000 + i, N=c["N"], C_in=c["C_in"], H=c["H"], W=c["W"], C_out=c["C_out"], k=c["k"])
+        b = p["b"] if c["bias"] else None
+        y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(b))
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy(), O.conv2d_relu_hswish(p["x"], p["w"], b), f"sweep conv2d {c}")
+
+
+def test_random_shape_sweep_conv3d(cce):
+    def draw(rng):
+        k = int(rng.choice([1, 3]))
+        lo, hi = [(-1.0, 1.0), (-1.0, 1.0), (-2.0, 1.5)][int(rng.integers(0, 3))]
+        return dict(N=int(rng.integers(1, 3)), C_in=int(rng.choice([4, 8, 16])), C_out=int(rng.choice([16, 32, 64])),
+                    k=k, D=int(rng.integers(k, 7)), H=int(rng.integers(k, 25)), W=int(rng.integers(k, 25)),
+                    slope=float(rng.choice([0.2, 0.05])), lo=lo, hi=hi)
+    for i, c in enumerate(_sweep_cases(2025, 16, draw)):
+        print(f"sweep conv3d case {i}: {c}", flush=True)
+        p = make_inputs(CONV3D, seed=3100 + i, N=c["N"], C_in=c["C_in"], D=c["D"], H=c["H"], W=c["W"],
+                        C_out=c["C_out"], k=c["k"])
+        s = (p["s"] * 20).astype(np.float32)
+        y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(s), c["slope"], c["lo"], c["hi"])
+        torch.cuda.synchronize()
+        ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], s, slope=c["slope"], lo=c["lo"], hi=c["hi"])
+        assert_close(y.cpu().numpy(), ref, f"sweep conv3d {c}")
+
+
+def test_random_shape_sweep_convT(cce):
+    def draw(rng):
+        return dict(N=int(rng.integers(1, 3)), C_in=int(8 * rng.integers(1, 9)), C_out=int(rng.choice([16, 32, 64])),
+                    H=int(rng.integers(2, 41)), W=int(rng.integers(2, 41)), bias=bool(rng.random() < 0.8))
+    for i, c in enumerate(_sweep_cases(2026, 12, draw)):
+        print(f"sweep convT case {i}: {c}", flush=True)
+        p = make_inputs(CONVT, seed=3200 + i, N=c["N"], C_in=c["C_in"], H=c["H"], W=c["W"], C_out=c["C_out"], k=3)
+        b = p["b"] if c["bias"] else None
+        y = cce.convT2d_pool_htanh_mean_tanh(dev(p["x"]), dev(p["w"]), dev(b))
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy()[:, :, 0, 0], O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], b), f"sweep convT {c}")
+
+
+def test_random_shape_sweep_tails(cce):
+    def draw_pool(rng):
+        pk = int(rng.integers(1, 4))
+        return dict(N=int(rng.integers(1, 3)), C=int(rng.integers(1, 6)), H=int(rng.integers(pk, 40)),
+                    W=int(rng.integers(pk, 40)), pk=pk, ps=int(rng.integers(1, 4)))
+    for i, c in enumerate(_sweep_cases(2027, 12, draw_pool)):
+        print(f"sweep pool tail case {i}: {c}", flush=True)
+        p = make_inputs(TAIL_POOL, seed=3300 + i, N=c["N"], C=c["C"], H=c["H"], W=c["W"])
+        y = cce.pool_htanh_mean_tanh(dev(p["z"]), pool_k=c["pk"], pool_s=c["ps"])
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy()[:, :, 0, 0], O.pool_htanh_mean_tanh(p["z"], pk=c["pk"], ps=c["ps"]),
+                     f"sweep pool tail {c}")
+
+    def draw_elt(rng):
+        return dict(N=int(rng.integers(1, 4)), C=int(rng.integers(1, 9)), D=int(rng.integers(1, 4)),
+                    H=int(rng.integers(1, 12)), W=int(rng.integers(1, 20)))
+    for i, c in enumerate(_sweep_cases(2028, 12, draw_elt)):
+        print(f"sweep elementwise tail case {i}: {c}", flush=True)
+        p = make_inputs(TAIL_GELU, seed=3400 + i, **c)
+        s = (p["s"] * 20).astype(np.float32)
+        y = cce.lrelu_add_clamp_gelu(dev(p["z"]), dev(s), 0.2, -1.0, 1.0)
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy(), O.lrelu_add_clamp_gelu_array(p["z"], s), f"sweep elementwise tail {c}")
