@@ -545,6 +545,36 @@ def test_elementwise_tail_plane_longer_than_2_31(cce):
     assert_close(got, ref, "elementwise tail, plane longer than 2^31")
 
 
+@pytest.mark.parametrize("quads", [2 ** 31 - 4, 2 ** 31 + 4])
+def test_elementwise_tail_flat_path_limit(cce, quads):
+    """The flat 16-byte path of the elementwise tail takes arrays of fewer than
+    2^31 quads; from 2^31 on, the per-plane path does.  Both sides of that
+    limit, in place (y = z), on two planes of 2 * quads floats (34 GB), built
+    by tiling a seeded draw on the GPU; sampled elements (both ends, the
+    plane boundary, the 2^31-quad boundary) against the oracle."""
+    C, S = 2, 2 * quads
+    small = make_inputs(TAIL_GELU, seed=84, N=1, C=C, D=1, H=1, W=2 ** 23)
+    zs = dev(small["z"]).reshape(-1)
+    z = zs.repeat((C * S + zs.numel() - 1) // zs.numel())[:C * S].reshape(1, C, S)
+    del zs
+    total = C * S
+    idx = np.unique(np.concatenate([sample_indices(total, 4000, 84), np.arange(S - 64, S + 64),
+                                    np.arange(min(4 * 2 ** 31, total) - 64, min(4 * 2 ** 31, total)),
+                                    np.arange(total - 64, total)]))
+    zg = gather(z, idx)
+    y = cce.lrelu_add_clamp_gelu(z, dev(small["s"]), 0.2, -1.0, 1.0, out=z)
+    torch.cuda.synchronize()
+    got = gather(y, idx)
+    del z, y
+    torch.cuda.empty_cache()
+    ch = idx // S
+    ref = np.empty(idx.shape[0])
+    for c in range(C):
+        m = ch == c
+        ref[m] = O.lrelu_add_clamp_gelu_array(zg[m].reshape(1, 1, -1), small["s"][c:c + 1])[0, 0]
+    assert_close(got, ref, f"elementwise tail in place, {quads} quads")
+
+
 def off(a=None, shape=None):
     """A GPU tensor (a copy of `a`, or zeros of `shape`) whose data pointer is
     4 bytes past a 16-byte boundary: 4-byte aligned, as the ABI requires, but
