@@ -68,6 +68,15 @@ MUTANTS = {
     "conv3d_model_channel_of_s": [(
         "* Wo + ww] =\n                oracle_lrelu_add_clamp_gelu(v, (double)s[o],",
         "* Wo + ww] =\n                oracle_lrelu_add_clamp_gelu(v, (double)s[(o + 1) % C_out],")],
+    "conv2d_sampled_index_decode": [(
+        "    int h = (int)(q % Ho); q /= Ho;\n    int o = (int)(q % C_out); q /= C_out;",
+        "    int o = (int)(q % C_out); q /= C_out;\n    int h = (int)(q % Ho); q /= Ho;")],
+    "conv3d_sampled_index_decode": [(
+        "    int d = (int)(q % Do); q /= Do;\n    int o = (int)(q % C_out); q /= C_out;",
+        "    int o = (int)(q % C_out); q /= C_out;\n    int d = (int)(q % Do); q /= Do;")],
+    "convT_sampled_image_channel_decode": [(
+        "int n = (int)(nc_idx[j] / C_out), o = (int)(nc_idx[j] % C_out);",
+        "int n = (int)(nc_idx[j] % N), o = (int)(nc_idx[j] / N);")],
     "f32_tail_mean_divisor": [("y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)PW));",
                                "y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)(PW + 1)));")],
 }

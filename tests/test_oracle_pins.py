@@ -157,7 +157,10 @@ def test_conv2d_relu_hswish_matches_torch_and_sampling():
     y = O.conv2d_relu_hswish(x, w, b)
     ref = F.hardswish(F.relu(F.conv2d(_t64(x), _t64(w), _t64(b)))).numpy()
     np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
-    idx = np.array([0, 1, 77, y.size // 2, y.size - 1])
+    # every output, in shuffled order: a handful of indices does not pin the
+    # index decoding (the last index decodes the same in any order, and many
+    # outputs are zero after the ReLU)
+    idx = np.random.default_rng(3).permutation(y.size)
     np.testing.assert_array_equal(O.conv2d_relu_hswish_at(x, w, b, idx), y.reshape(-1)[idx])
 
 
@@ -296,7 +299,7 @@ def test_conv3d_model_matches_torch_and_sampling():
     ref = F.gelu(torch.clamp(F.leaky_relu(z, 0.2) + _t64(s).view(1, -1, 1, 1, 1), -1, 1)).numpy()
     np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
     assert y.min() >= GELU_MIN - 1e-12 and y.max() <= 0.8413447460685429 + 1e-12
-    idx = np.array([0, 5, y.size // 3, y.size - 1])
+    idx = np.random.default_rng(4).permutation(y.size)  # every output, shuffled
     np.testing.assert_array_equal(O.conv3d_lrelu_add_clamp_gelu_at(x, w, b, s, idx), y.reshape(-1)[idx])
 
 
@@ -420,7 +423,7 @@ def test_convT_model_matches_torch(hw):
     assert y.shape == ref.shape[:2]
     np.testing.assert_allclose(y, ref[:, :, 0, 0], rtol=0, atol=1e-13)
     assert np.all(np.abs(y) <= math.tanh(1) + 1e-15)
-    idx = np.array([0, 63, 64, 127])
+    idx = np.random.default_rng(5).permutation(y.size)  # every (image, channel), shuffled
     np.testing.assert_array_equal(O.convT2d_pool_htanh_mean_tanh_at(x, w, b, idx), y.reshape(-1)[idx])
 
 
