@@ -77,6 +77,14 @@ MUTANTS = {
     "convT_sampled_image_channel_decode": [(
         "int n = (int)(nc_idx[j] / C_out), o = (int)(nc_idx[j] % C_out);",
         "int n = (int)(nc_idx[j] % N), o = (int)(nc_idx[j] / N);")],
+    "clamp_lower_bound": [("if (v < lo) v = lo;", "if (v < lo) v = hi;")],
+    "pool_running_max_starts_at_zero": [("      double m = z[(size_t)(ph * ps) * Wo + (pw * ps)];",
+                                         "      double m = 0.0;")],
+    "mean_over_unpooled_count": [("  return tanh(sum / ((double)PH * (double)PW));",
+                                  "  return tanh(sum / ((double)Ho * (double)Wo));")],
+    "tanh_dropped": [("  return tanh(sum / ((double)PH * (double)PW));", "  return sum / ((double)PH * (double)PW);")],
+    "conv3d_weight_taps_swapped": [("double wv = w[((((size_t)o * C_in + i) * k + kd) * k + kh) * k + kw];",
+                                    "double wv = w[((((size_t)o * C_in + i) * k + kh) * k + kd) * k + kw];")],
     "f32_tail_mean_divisor": [("y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)PW));",
                                "y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)(PW + 1)));")],
 }
