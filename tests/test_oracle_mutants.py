@@ -90,30 +90,47 @@ MUTANTS = {
 }
 
 
-def _build_and_run_pins(tmp_path: Path, text: str):
-    src = tmp_path / "oracle_copy.c"
-    so = tmp_path / "liboracle_copy.so"
+def _build_and_run_pins(workdir: Path, text: str):
+    workdir.mkdir(parents=True, exist_ok=True)
+    src = workdir / "oracle_copy.c"
+    so = workdir / "liboracle_copy.so"
     src.write_text(text)
     subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", str(so), str(src), "-lm"],
                    check=True, capture_output=True)
-    env = dict(os.environ, CCE_ORACLE_LIB=str(so), OMP_NUM_THREADS=os.environ.get("OMP_NUM_THREADS", "4"))
+    env = dict(os.environ, CCE_ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
     return subprocess.run([sys.executable, "-m", "pytest", str(PINS), "-x", "-q", "-p", "no:cacheprovider",
                            "-m", "not gpu"], cwd=str(ROOT), env=env, capture_output=True, text=True,
                           timeout=600)
 
 
-def test_control_copy_passes_the_pins(tmp_path):
-    res = _build_and_run_pins(tmp_path, SRC.read_text())
-    assert res.returncode == 0, res.stdout[-3000:] + res.stderr[-2000:]
-
-
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_planted_mistake(tmp_path, name):
+def _mutant_text(name):
     text = SRC.read_text()
     for old, new in MUTANTS[name]:
         assert text.count(old) == 1, f"{name}: anchor not found exactly once in oracle.c: {old!r}"
         text = text.replace(old, new)
-    res = _build_and_run_pins(tmp_path, text)
+    return text
+
+
+@pytest.fixture(scope="module")
+def pin_runs(tmp_path_factory):
+    """The pin suite run against the control copy and every mutant, four at a
+    time (each run is its own process with two OpenMP threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+    base = tmp_path_factory.mktemp("oracle_copies")
+    jobs = [("control", SRC.read_text())] + [(n, _mutant_text(n)) for n in sorted(MUTANTS)]
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        results = list(pool.map(lambda j: (j[0], _build_and_run_pins(base / j[0], j[1])), jobs))
+    return dict(results)
+
+
+def test_control_copy_passes_the_pins(pin_runs):
+    res = pin_runs["control"]
+    assert res.returncode == 0, res.stdout[-3000:] + res.stderr[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(pin_runs, name):
+    res = pin_runs[name]
     tail = res.stdout.strip().splitlines()[-1] if res.stdout.strip() else ""
     # A pin must fail (an assertion), not the test run itself (collection or import errors).
     assert res.returncode == 1 and " failed" in tail and "error" not in tail, \
