@@ -85,6 +85,15 @@ MUTANTS = {
     "tanh_dropped": [("  return tanh(sum / ((double)PH * (double)PW));", "  return sum / ((double)PH * (double)PW);")],
     "conv3d_weight_taps_swapped": [("double wv = w[((((size_t)o * C_in + i) * k + kd) * k + kh) * k + kw];",
                                     "double wv = w[((((size_t)o * C_in + i) * k + kh) * k + kd) * k + kw];")],
+    "pool_tail_plane_order": [("oracle_pool_htanh_mean_tanh_plane(z + ((size_t)n * C + c) * H * W, H, W, pk, ps, lo, hi);",
+                               "oracle_pool_htanh_mean_tanh_plane(z + ((size_t)c * N + n) * H * W, H, W, pk, ps, lo, hi);")],
+    "f32_tail_plane_order": [("const float *zp = z + ((size_t)n * C + c) * H * W;",
+                              "const float *zp = z + ((size_t)c * N + n) * H * W;")],
+    "convT_gather_bias_dropped": [(
+        "int ww) {\n  double acc = bias_of(b, o);\n  for (int i = 0; i < C_in; ++i)\n    for (int kh = 0; kh < k; ++kh) {\n      int th",
+        "int ww) {\n  double acc = 0.0; (void)b;\n  for (int i = 0; i < C_in; ++i)\n    for (int kh = 0; kh < k; ++kh) {\n      int th")],
+    "convT_scatter_flipped_positions": [("int oh = ih * stride - pad + kh, ow = iw * stride - pad + kw;",
+                                         "int oh = ih * stride + pad - kh, ow = iw * stride + pad - kw;")],
     "f32_tail_mean_divisor": [("y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)PW));",
                                "y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)(PW + 1)));")],
 }
