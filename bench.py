@@ -5,15 +5,17 @@
 
 One step is one call of the headline workload's fused operator on one batch
 of seeded synthetic input already resident in device memory (the default
-headline is Conv2d 3x3 8->64 + ReLU + HardSwish at N = 128, 128 x 128).
+headline is the largest workload: ConvTranspose2d 3x3 64->64 + MaxPool 2x2 +
+Hardtanh + mean + tanh at N = 128, 256 x 256).
 S seconds of untimed pre-warm calls (an idle GPU needs a moment of load
 before its clocks settle), W untimed warm-up steps, then exactly K timed
 steps bracketed by device synchronisations; HIP events on the stream the kernels run on give the
 per-launch kernel time.  Rank 0 prints one JSON line with the headline
 throughput (GFLOP/s of the convolution's multiply-adds, 2 FLOP each), the
-roofline of the dominant kernel, the CPU oracle's throughput on a bounded
-sample (a baseline, not a target) and, under "ops", the same measurement for
-every fused workload.
+roofline of the dominant kernel, the CPU oracle's throughput (a baseline, not
+a target) and, under "ops", the same measurement for every workload.  Every
+workload's whole output is also compared with the oracle's
+(gpu_error_vs_oracle); --no-cpu-baseline skips the oracle.
 
 Only one GPU exists per box and nothing here is distributed: --gpus above 1
 exits with a message.
@@ -39,7 +41,7 @@ from conv_inputs import (CONV2D, CONV3D, CONVT, TAIL_GELU, TAIL_POOL, WORKLOADS,
 METRIC = "fused conv+epilogue ms per call, GFLOP/s & % of fp32/HBM roofline (1 MI355X)"
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
-HEADLINE = "conv2d_relu_hswish_n128"
+HEADLINE = "convT2d_pool_htanh_mean_tanh_n128"  # the largest workload that fits one GPU
 
 KERNEL_SOURCES = {
     CONV2D: "conv2d_relu_hswish.hip",
@@ -357,9 +359,12 @@ def per_call_times(torch, fn, calls, evict=None):
 
 
 def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0, cold_calls=0, keep_output=False):
+    """Time one workload; with keep_output, also return its host inputs and
+    the last call's result (out["inputs"], out["y"]) for the oracle check."""
     shape, p = workload_inputs(name, seed)
     d = device_inputs(torch, cce, shape, p)
-    del p
+    if not keep_output:
+        del p
     fn = run_op(cce, shape, d)
     # Bring the GPU out of its idle clocks first: a freshly idle MI355X needs a
     # fraction of a second of load before kernel times settle.
@@ -412,6 +417,7 @@ def time_workload(torch, cce, name, steps, warmup, seed, prewarm_s=0.0, cold_cal
         fn()
         torch.cuda.synchronize()
         out["y"] = d["y"].cpu().numpy()
+        out["inputs"] = p
     del d
     torch.cuda.empty_cache()
     return shape, out
@@ -454,89 +460,98 @@ def unfused_torch(torch, name, steps, seed):
     return round(ms, 5)
 
 
-def error_vs_oracle(gpu, ref):
-    """Max abs and rel error of the GPU result against the oracle over the
-    sampled outputs, and how many exceed the 1e-4 + 1e-4 |ref| tolerance."""
-    g = np.asarray(gpu, np.float64).reshape(-1)
-    r = np.asarray(ref, np.float64).reshape(-1)
-    err = np.abs(g - r)
-    rel = err / np.maximum(np.abs(r), 1e-30)
-    return {"outputs": int(r.size), "max_abs": float(err.max()), "max_rel_where_abs_ref_ge_1e-3":
-            float(rel[np.abs(r) >= 1e-3].max()) if np.any(np.abs(r) >= 1e-3) else 0.0,
-            "over_tolerance": int(np.count_nonzero(err > 1e-4 + 1e-4 * np.abs(r))),
-            "finite": bool(np.all(np.isfinite(g)))}
+class ErrorVsOracle:
+    """Running comparison of GPU outputs with the oracle's, chunk by chunk:
+    max abs error, max rel error where |ref| >= 1e-3, and how many outputs
+    exceed the 1e-4 + 1e-4 |ref| tolerance."""
+
+    def __init__(self):
+        self.outputs, self.max_abs, self.max_rel, self.over, self.finite = 0, 0.0, 0.0, 0, True
+
+    def add(self, gpu, ref):
+        g = np.asarray(gpu, np.float64).reshape(-1)
+        r = np.asarray(ref, np.float64).reshape(-1)
+        err = np.abs(g - r)
+        big = np.abs(r) >= 1e-3
+        self.outputs += int(r.size)
+        self.max_abs = max(self.max_abs, float(err.max()) if err.size else 0.0)
+        if big.any():
+            self.max_rel = max(self.max_rel, float((err[big] / np.abs(r[big])).max()))
+        self.over += int(np.count_nonzero(~(err <= 1e-4 + 1e-4 * np.abs(r))))
+        self.finite = self.finite and bool(np.all(np.isfinite(g)))
+
+    def result(self):
+        return {"outputs": self.outputs, "max_abs": self.max_abs, "max_rel_where_abs_ref_ge_1e-3": self.max_rel,
+                "over_tolerance": self.over, "finite": self.finite}
 
 
-def cpu_baseline(name, seed, budget_s=12.0, gpu_y=None):
-    """The CPU oracle (double precision, OpenMP over all host cores) timed on a
-    bounded sample of the workload, scaled to GFLOP/s of the same algorithmic
-    count.  With the GPU's result `gpu_y`, the same sample also gives the GPU's
-    error against the oracle."""
+def oracle_check(name, shape, p, gpu_y, budget_s=90.0, seed=0):
+    """The CPU oracle (double precision, OpenMP over the host's cores) over
+    the whole output of a workload, compared with the GPU's result `gpu_y`
+    output by output.  Only the oracle's own compute is timed, and reported
+    in the headline metric's unit (GFLOP/s of the convolution's
+    multiply-adds; GB/s of the algorithmic bytes for the epilogue-only
+    operators) as a CPU baseline.  Convolution and elementwise outputs are
+    computed a few images at a time to bound host memory.  For the
+    transposed convolution the first `cores` (image, channel) outputs
+    estimate the whole run; if that exceeds `budget_s` seconds a random
+    subset that fits the budget is computed instead (and named as such)."""
     import oracle as O
-    shape, p = workload_inputs(name, seed)
     op = shape["op"]
     cores = O.num_threads()
-    rng = np.random.default_rng(seed)
-    if op in HBM_BOUND:
-        # whole images of the epilogue-only operators, reported as GB/s of the same byte count
-        per_image = work_counts(dict(shape, N=1))["bytes"]
-        run = ((lambda z: O.pool_htanh_mean_tanh(z, shape["pool_k"], shape["pool_s"], shape["lo"], shape["hi"]))
-               if op == TAIL_POOL else
-               (lambda z: O.lrelu_add_clamp_gelu_array(z, p["s"], shape["slope"], shape["lo"], shape["hi"])))
+    acc = ErrorVsOracle()
+    spent = 0.0
+
+    def timed(fn, *a, **k):
+        nonlocal spent
         t = time.perf_counter()
-        run(np.ascontiguousarray(p["z"][:1]))
-        one = time.perf_counter() - t
-        n = int(max(1, min(shape["N"], budget_s / max(one, 1e-6))))
-        zs = np.ascontiguousarray(p["z"][:n])
-        t = time.perf_counter()
-        ref = run(zs)
-        dt = time.perf_counter() - t
-        res = {"value": round(per_image * n / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
-               "kind": "oracle", "sample": f"{n} of {shape['N']} images", "seconds": round(dt, 3)}
-        if gpu_y is not None:
-            g = gpu_y[:n, :, 0, 0] if op == TAIL_POOL else gpu_y[:n]
-            res["gpu_error"] = error_vs_oracle(g, ref)
-        return res
-    if op in (CONV2D, CONV3D):
-        # whole images, as many as fit the time budget (at least one)
-        per_image = work_counts(dict(shape, N=1))["fma"]
-        t = time.perf_counter()
-        x1 = np.ascontiguousarray(p["x"][:1])
-        if op == CONV2D:
-            O.conv2d_relu_hswish(x1, p["w"], p["b"])
-        else:
-            O.conv3d_lrelu_add_clamp_gelu(x1, p["w"], p["b"], p["s"], shape["slope"], shape["lo"], shape["hi"])
-        one = time.perf_counter() - t
-        n = int(max(1, min(shape["N"], budget_s / max(one, 1e-6))))
-        xs = np.ascontiguousarray(p["x"][:n])
-        t = time.perf_counter()
-        if op == CONV2D:
-            ref = O.conv2d_relu_hswish(xs, p["w"], p["b"])
-        else:
-            ref = O.conv3d_lrelu_add_clamp_gelu(xs, p["w"], p["b"], p["s"], shape["slope"], shape["lo"],
-                                                shape["hi"])
-        dt = time.perf_counter() - t
-        sample = f"{n} of {shape['N']} images, full output"
-        fma = per_image * n
-        gpu_part = None if gpu_y is None else gpu_y[:n]
+        r = fn(*a, **k)
+        spent += time.perf_counter() - t
+        return r
+
+    N = shape["N"]
+    sample = "every output"
+    if op in (CONV2D, CONV3D, TAIL_GELU):
+        step = 32 if op == CONV2D else 8
+        for n0 in range(0, N, step):
+            if op == CONV2D:
+                ref = timed(O.conv2d_relu_hswish, np.ascontiguousarray(p["x"][n0:n0 + step]), p["w"], p["b"])
+            elif op == CONV3D:
+                ref = timed(O.conv3d_lrelu_add_clamp_gelu, np.ascontiguousarray(p["x"][n0:n0 + step]), p["w"],
+                            p["b"], p["s"], shape["slope"], shape["lo"], shape["hi"])
+            else:
+                ref = timed(O.lrelu_add_clamp_gelu_array, np.ascontiguousarray(p["z"][n0:n0 + step]), p["s"],
+                            shape["slope"], shape["lo"], shape["hi"])
+            acc.add(gpu_y[n0:n0 + step], ref)
+        work = work_counts(shape)
+    elif op == TAIL_POOL:
+        ref = timed(O.pool_htanh_mean_tanh, p["z"], shape["pool_k"], shape["pool_s"], shape["lo"], shape["hi"])
+        acc.add(gpu_y[:, :, 0, 0], ref)
+        work = work_counts(shape)
     else:
-        per_plane = work_counts(shape)["fma"] // (shape["N"] * shape["C_out"])
-        t = time.perf_counter()
-        O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], np.arange(cores))
-        one = (time.perf_counter() - t) / cores
-        count = int(max(cores, min(shape["N"] * shape["C_out"], budget_s / max(one, 1e-6))))
-        idx = rng.choice(shape["N"] * shape["C_out"], size=count, replace=False)
-        t = time.perf_counter()
-        ref = O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], idx)
-        dt = time.perf_counter() - t
-        sample = f"{count} of {shape['N'] * shape['C_out']} (image, channel) outputs"
-        fma = per_plane * count
-        gpu_part = None if gpu_y is None else gpu_y.reshape(-1)[idx]
-    res = {"value": round(2 * fma / dt / 1e9, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
-           "sample": sample, "seconds": round(dt, 3)}
-    if gpu_part is not None:
-        res["gpu_error"] = error_vs_oracle(gpu_part, ref)
-    return res
+        total = N * shape["C_out"]
+        gy = gpu_y.reshape(-1)
+        first = np.arange(min(cores, total))
+        acc.add(gy[first], timed(O.convT2d_pool_htanh_mean_tanh_at, p["x"], p["w"], p["b"], first))
+        estimate = spent * total / max(1, first.size)
+        if estimate <= budget_s:
+            rest = np.arange(first.size, total)
+        else:
+            count = int(max(0, budget_s / spent * first.size - first.size))
+            rest = np.sort(np.random.default_rng(seed).choice(np.arange(first.size, total), size=count,
+                                                              replace=False))
+            sample = f"{first.size + count} of {total} (image, channel) outputs"
+        if rest.size:
+            acc.add(gy[rest], timed(O.convT2d_pool_htanh_mean_tanh_at, p["x"], p["w"], p["b"], rest))
+        per_output = work_counts(shape)["fma"] // total
+        work = {"flop": 2 * per_output * (first.size + rest.size), "bytes": 0}
+    if op in HBM_BOUND:
+        value, unit = work["bytes"] / spent / 1e9, "GB/s"
+    else:
+        value, unit = work["flop"] / spent / 1e9, "GFLOP/s"
+    base = {"value": round(value, 3), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{sample} of {name}", "seconds": round(spent, 3)}
+    return base, acc.result()
 
 
 def main():
@@ -607,31 +622,53 @@ def main():
         print(json.dumps({"layer_shapes": rows, "steps": args.steps, "warmup": args.warmup}), flush=True)
         return
 
+    check = not args.no_cpu_baseline
+
+    def report(name, r):
+        print(f"# {name}: {r['ms_per_call']:.4f} ms/call, {r['gflops']:.1f} GFLOP/s, {r['gbs']:.1f} GB/s, "
+              f"{r['roofline']['frac']:.3f} of the {r['roofline']['bound']} roofline", file=sys.stderr, flush=True)
+
+    def with_oracle(name, shape, r):
+        """Every output of the workload against the CPU oracle (unless
+        --no-cpu-baseline); frees the host copies afterwards."""
+        gy, p = r.pop("y", None), r.pop("inputs", None)
+        if gy is None:
+            return
+        base, err = oracle_check(name, shape, p, gy, seed=args.seed)
+        r["oracle"], r["gpu_error_vs_oracle"] = base, err
+        print(f"# {name}: oracle {base['seconds']:.1f} s on {base['cores']} threads ({base['sample']}); "
+              f"GPU max abs error {err['max_abs']:.2e}, {err['over_tolerance']} of {err['outputs']} "
+              f"outputs over tolerance", file=sys.stderr, flush=True)
+
     shape, head = time_workload(torch, cce, args.workload, args.steps, args.warmup, args.seed,
-                                args.prewarm, args.cold_calls, keep_output=not args.no_cpu_baseline)
-    gpu_y = head.pop("y", None)
-    print(f"# {args.workload}: {head['ms_per_call']:.4f} ms/call, {head['gflops']:.1f} GFLOP/s, "
-          f"{head['gbs']:.1f} GB/s, {head['roofline']['frac']:.3f} of the {head['roofline']['bound']} roofline",
-          file=sys.stderr, flush=True)
+                                args.prewarm, args.cold_calls, keep_output=check)
+    report(args.workload, head)
     ops = {}
     if args.ops == "all":
         for name in WORKLOADS:
             if name == args.workload:
                 r = head
             else:
-                _, r = time_workload(torch, cce, name, max(3, min(args.steps, 50)), min(args.warmup, 10),
-                                     args.seed, min(args.prewarm, 0.5), min(args.cold_calls, 10))
-                print(f"# {name}: {r['ms_per_call']:.4f} ms/call, {r['gflops']:.1f} GFLOP/s, "
-                      f"{r['gbs']:.1f} GB/s, {r['roofline']['frac']:.3f} of the "
-                      f"{r['roofline']['bound']} roofline", file=sys.stderr, flush=True)
+                shp, r = time_workload(torch, cce, name, max(3, min(args.steps, 50)), min(args.warmup, 10),
+                                       args.seed, min(args.prewarm, 0.5), min(args.cold_calls, 10),
+                                       keep_output=check)
+                report(name, r)
+                with_oracle(name, shp, r)
             ops[name] = {"ms_per_call": round(r["ms_per_call"], 5), "gflops": round(r["gflops"], 1),
                          "gbs": round(r["gbs"], 1), "roofline_bound": r["roofline"]["bound"],
-                         "roofline_frac": r["roofline"]["frac"],
+                         "roofline_frac": r["roofline"]["frac"], "traffic": r["roofline"]["traffic"],
                          "hbm_frac": r["hbm_frac"], "hot": r["hot"]}
             if "cold" in r:
                 ops[name]["cold"] = r["cold"]
             if name in PAGES_ESTIMATE:
                 ops[name]["pages_estimate"] = PAGES_ESTIMATE[name]
+    # The headline's oracle run last: the GPU is idle meanwhile, and the other
+    # workloads' timings are not delayed by it.
+    with_oracle(args.workload, shape, head)
+    for name in ops:
+        r = head if name == args.workload else None
+        if r is not None and "oracle" in r:
+            ops[name]["oracle"], ops[name]["gpu_error_vs_oracle"] = r["oracle"], r["gpu_error_vs_oracle"]
 
     line = {
         "metric": METRIC,
@@ -673,9 +710,9 @@ def main():
             print(f"# unfused torch {name}: {ms:.4f} ms/call ({ms / fused:.2f}x the fused kernel)",
                   file=sys.stderr, flush=True)
         line["unfused_torch"] = ctx
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload, args.seed, gpu_y=gpu_y)
-        line["gpu_error_vs_oracle"] = line["cpu_baseline"].pop("gpu_error", None)
+    if "oracle" in head:
+        line["cpu_baseline"] = head["oracle"]
+        line["gpu_error_vs_oracle"] = head["gpu_error_vs_oracle"]
     if ops:
         line["ops"] = ops
     print(json.dumps(line), flush=True)

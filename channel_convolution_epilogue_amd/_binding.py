@@ -197,13 +197,14 @@ def convT2d_pool_htanh_mean_tanh_workspace_bytes(N, C_in, H, W, C_out, k=3, stri
 
 
 def _workspace(device, stream: int, nbytes: int):
-    """A zero-initialised workspace cached per (device, stream); the kernel
-    leaves it valid for the next call, so it is zeroed only when (re)allocated."""
+    """A workspace cached per (device, stream) and grown when a call needs
+    more.  The call initialises every workspace byte it reads, so the cached
+    buffer serves later calls of any shape without being cleared."""
     import torch
     key = (device.index, stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -214,7 +215,7 @@ def convT2d_pool_htanh_mean_tanh(x, w, b=None, stride=1, padding=1, pool_k=2, po
 
     x [N, C_in, H, W], w [C_in, C_out, k, k], b [C_out] or None.  `workspace`
     (optional) is a uint8 GPU tensor of at least
-    convT2d_pool_htanh_mean_tanh_workspace_bytes(...) bytes, zeroed once.
+    convT2d_pool_htanh_mean_tanh_workspace_bytes(...) bytes, any contents.
     """
     import torch
     L = load()

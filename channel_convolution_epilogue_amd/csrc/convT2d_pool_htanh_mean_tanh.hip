@@ -27,8 +27,9 @@
 //    lane -> wave (cross-lane shuffles) -> workgroup (LDS).
 //  * Each workgroup stores its 64 partial sums and bumps a per-image counter
 //    (agent-scope acquire/release); the workgroup that completes an image
-//    adds that image's partials in a fixed order, applies mean and tanh, and
-//    resets the counter.  The result is deterministic.
+//    adds that image's partials in a fixed order and applies mean and tanh.
+//    The result is deterministic.  A small kernel launched just before the
+//    main one zeroes the counters and writes the prepared weight.
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
 
@@ -64,7 +65,7 @@ struct ConvTArgs {
   const float *__restrict__ w;
   const float *__restrict__ b;
   float *__restrict__ y;
-  unsigned *tickets;  // [N] per-image completion counters (zero between calls)
+  unsigned *tickets;  // [N] per-image completion counters (zeroed per call)
   float *partials;    // [N][tiles_per_image][C_out]
   const float *wprep; // prepared weight, nchunk x WS_FLOATS
   int C_in, nchunk;   // nchunk = C_in / CC
@@ -169,15 +170,25 @@ __device__ __forceinline__ void store_chunk(float *xs, float *ws, int tid, const
   }
 }
 
-// Weight preparation (once per call, C_in x C_out x 9 floats): the flipped,
-// channel-swapped kernel in exactly the LDS B-operand order of every chunk,
-//   wprep[c][cb][tap'][lane][nt] = W[8c + 4cb + lane/16][16nt + lane%16][8 - tap'],
-// where tap' = 3 kh' + kw' and W's tap index 3 kh + kw = 8 - tap'.
+// Per-call preparation of the workspace, launched on the same stream just
+// before the main kernel:
+//  * the flipped, channel-swapped kernel (C_in x C_out x 9 floats) in exactly
+//    the LDS B-operand order of every chunk,
+//      wprep[c][cb][tap'][lane][nt] = W[8c + 4cb + lane/16][16nt + lane%16][8 - tap'],
+//    where tap' = 3 kh' + kw' and W's tap index 3 kh + kw = 8 - tap';
+//  * the N per-image completion counters set to zero.
+// Every workspace byte the main kernel reads is thus written by this call
+// (the per-tile partials by the main kernel itself before they are read),
+// so the workspace needs no initial contents, and a workspace last used by a
+// call of another shape -- whose prepared weight may cover this call's
+// counters -- is as good as a fresh one.
 template <class OC>
 __global__ __launch_bounds__(THREADS) void convT_prepare_weight_kernel(const float *__restrict__ w,
                                                                       float *__restrict__ wprep,
-                                                                      int total) {
+                                                                      int total, unsigned *tickets,
+                                                                      int N) {
   const int p = blockIdx.x * THREADS + threadIdx.x;
+  if (p < N) tickets[p] = 0u;
   if (p >= total) return;
   const int nt = p % OC::NT, lane = (p / OC::NT) & 63, rest = p / (OC::NT * 64);
   const int tap = rest % 9, ccb = rest / 9;  // rest = (c * 2 + cb) * 9 + tap, ccb = c * 2 + cb
@@ -312,8 +323,6 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
     for (int part = 0; part < PARTS; ++part) tot += red[part * CO + tid];
     a.y[(size_t)n * CO + tid] = tanhf(tot * a.inv_count);
   }
-  if (tid == 0)
-    __hip_atomic_store(&a.tickets[n], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr size_t kTicketAlign = 256;
@@ -334,10 +343,11 @@ size_t ticket_bytes(int N) {
 size_t wprep_bytes(int C_in, int C_out) { return (size_t)C_in * C_out * 9 * sizeof(float); }
 
 template <class OC, int NCH>
-int launch_for(ConvTArgs a, const float *w, float *wprep, long long grid, hipStream_t stream) {
+int launch_for(ConvTArgs a, const float *w, float *wprep, int N, long long grid, hipStream_t stream) {
   const int total = a.C_in * OC::CO * 9;
-  hipLaunchKernelGGL(convT_prepare_weight_kernel<OC>, dim3((total + THREADS - 1) / THREADS),
-                     dim3(THREADS), 0, stream, w, wprep, total);
+  const int prep_items = total > N ? total : N;
+  hipLaunchKernelGGL(convT_prepare_weight_kernel<OC>, dim3((prep_items + THREADS - 1) / THREADS),
+                     dim3(THREADS), 0, stream, w, wprep, total, a.tickets, N);
   if (launch_status() != CCE_OK) return CCE_ERR_LAUNCH;
   const bool vec = (a.W % 4 == 0) && ((uintptr_t)a.x % 16 == 0);
   if (vec)
@@ -389,11 +399,11 @@ int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const fl
   const long long grid = (long long)N * a.tiles_per_image;
   if (grid >= (1LL << 31)) return CCE_ERR_TOO_LARGE;
   switch (C_out) {
-    case 16: return launch_for<OutCh<16>, 0>(a, w, wprep, grid, stream);
-    case 32: return launch_for<OutCh<32>, 0>(a, w, wprep, grid, stream);
+    case 16: return launch_for<OutCh<16>, 0>(a, w, wprep, N, grid, stream);
+    case 32: return launch_for<OutCh<32>, 0>(a, w, wprep, N, grid, stream);
     default:
-      if (C_in == 64) return launch_for<OutCh<64>, 64 / CC>(a, w, wprep, grid, stream);
-      return launch_for<OutCh<64>, 0>(a, w, wprep, grid, stream);
+      if (C_in == 64) return launch_for<OutCh<64>, 64 / CC>(a, w, wprep, N, grid, stream);
+      return launch_for<OutCh<64>, 0>(a, w, wprep, N, grid, stream);
   }
 }
 

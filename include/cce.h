@@ -132,10 +132,11 @@ int conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const float *b, 
  *
  * Workspace: device memory of at least
  * convT2d_pool_htanh_mean_tanh_workspace_bytes(...) bytes, 256-byte
- * aligned, ALL ZERO before the first call that uses it.  Each call leaves it
- * in a state valid for the next call of any shape, so zero it once, when it
- * is allocated.  It holds per-image completion counters and per-tile
- * partial sums; one workspace serves one call at a time.
+ * aligned, with any contents: the call first writes everything it later
+ * reads there (per-image completion counters, the prepared weight, per-tile
+ * partial sums), on `stream`, so one workspace may serve calls of any shapes
+ * one after another.  One workspace serves one call at a time: calls that
+ * overlap in time (on different streams) need one workspace each.
  *
  * Supported: k = 3, stride = 1, pad = 1, pool_k = pool_s = 2; C_in a
  * multiple of 8 in [8, 512] and C_out in {16, 32, 64} (the page's layer is

@@ -79,7 +79,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_pool_htanh_mean_tanh_plane.restype = _c_dbl
         L.oracle_pool_htanh_mean_tanh_plane.argtypes = [_d] + [_c_int] * 4 + [_c_dbl] * 2
         L.oracle_pool_htanh_mean_tanh.argtypes = [_d, _d] + [_c_int] * 6 + [_c_dbl] * 2
-        L.oracle_pool_htanh_mean_tanh_f32.argtypes = [_f, _d] + [_c_int] * 6 + [_c_dbl] * 2
+        L.oracle_pool_htanh_mean_tanh_f32.argtypes = [_f, _d] + [_c_int] * 6 + [_c_dbl] * 2 + [_d, ctypes.c_int64]
+        L.oracle_convT2d_planes.argtypes = [_f, _f, _f, _d] + [_c_int] * 8
         L.oracle_lrelu_add_clamp_gelu_f32.argtypes = [_f, _f, _d, _c_int, _c_int, ctypes.c_int64] + [_c_dbl] * 3
         L.oracle_convT2d_pool_htanh_mean_tanh_at.argtypes = (
             [_f, _f, _f] + [_c_int] * 10 + [_c_dbl] * 2 + [_i64, ctypes.c_int64, _d, ctypes.c_int64, _d])
@@ -231,6 +232,18 @@ def convT2d_gather(x, w, b=None, stride=1, pad=1):
     return z
 
 
+def convT2d_planes(x, w, b=None, stride=1, pad=1):
+    """The transposed conv as the model path evaluates it (tap-major scatter
+    per output plane), [N, C_out, Ho, Wo] in double."""
+    N, C_in, H, W = x.shape
+    _, C_out, k, _ = w.shape
+    Ho, Wo = convT_out_size(H, k, stride, pad), convT_out_size(W, k, stride, pad)
+    z = np.empty((N, C_out, Ho, Wo), np.float64)
+    _check(lib().oracle_convT2d_planes(_fp(x), _fp(w), _fp(b), _dp(z), N, C_in, H, W, C_out, k,
+                                       stride, pad), "convT2d_planes")
+    return z
+
+
 def pool_htanh_mean_tanh_plane(z_plane, pk=2, ps=2, lo=-1.0, hi=1.0) -> float:
     z = np.ascontiguousarray(z_plane, dtype=np.float64)
     Ho, Wo = z.shape
@@ -267,8 +280,10 @@ def pool_htanh_mean_tanh(z, pk=2, ps=2, lo=-1.0, hi=1.0):
     N, C, H, W = z.shape
     y = np.empty((N, C), np.float64)
     if z.dtype == np.float32:
+        scratch = np.empty(max(1, num_threads()) * H * W, np.float64)
         _check(lib().oracle_pool_htanh_mean_tanh_f32(_fp(np.ascontiguousarray(z)), _dp(y), N, C, H, W,
-                                                     pk, ps, lo, hi), "pool_htanh_mean_tanh")
+                                                     pk, ps, lo, hi, _dp(scratch), scratch.shape[0]),
+               "pool_htanh_mean_tanh")
     else:
         zd = np.ascontiguousarray(z, dtype=np.float64)
         _check(lib().oracle_pool_htanh_mean_tanh(_dp(zd), _dp(y), N, C, H, W, pk, ps, lo, hi),

@@ -375,18 +375,61 @@ double oracle_pool_htanh_mean_tanh_plane(const double *z, int Ho, int Wo, int pk
   return tanh(sum / ((double)PH * (double)PW));
 }
 
+/* One (n, o) plane of the transposed conv, z[Ho][Wo], in the scatter form
+ * with the kernel taps outermost: start from the bias, then for each input
+ * channel i and tap (kh, kw) in turn, add the input plane x[n,i] times
+ * W[i,o,kh,kw] into the output at (ih*stride - pad + kh, iw*stride - pad + kw),
+ * dropping positions outside the output.  Each output receives its terms in
+ * ascending (i, kh, kw) order -- the order of the gather form above -- so the
+ * two evaluations give the same doubles (the tests pin that bit for bit); this
+ * order reads each input plane row by row. */
+static void convT2d_plane(const float *x, const float *w, const float *b, int C_in, int H, int W,
+                          int C_out, int k, int stride, int pad, int n, int o, double *z) {
+  int Ho = oracle_convT_out_size(H, k, stride, pad), Wo = oracle_convT_out_size(W, k, stride, pad);
+  for (size_t p = 0; p < (size_t)Ho * Wo; ++p) z[p] = bias_of(b, o);
+  for (int i = 0; i < C_in; ++i) {
+    const float *xp = x + ((size_t)n * C_in + i) * H * W;
+    for (int kh = 0; kh < k; ++kh)
+      for (int kw = 0; kw < k; ++kw) {
+        double wv = (double)w[(((size_t)i * C_out + o) * k + kh) * k + kw];
+        for (int ih = 0; ih < H; ++ih) {
+          int oh = ih * stride - pad + kh;
+          if (oh < 0 || oh >= Ho) continue;
+          for (int iw = 0; iw < W; ++iw) {
+            int ow = iw * stride - pad + kw;
+            if (ow < 0 || ow >= Wo) continue;
+            z[(size_t)oh * Wo + ow] += (double)xp[(size_t)ih * W + iw] * wv;
+          }
+        }
+      }
+  }
+}
+
 /* y[N][C_out] (= [N,C_out,1,1]) = tanh(mean(hardtanh(maxpool(convT2d(x))))),
- * the whole l2_p10 model.  The transposed conv is evaluated in its gather
- * form one (n, o) plane at a time (the tests pin gather == scatter). */
+ * the whole l2_p10 model, one (n, o) plane at a time. */
 static int convT_model_plane(const float *x, const float *w, const float *b, int C_in, int H,
                              int W, int C_out, int k, int stride, int pad, int pk, int ps,
                              double lo, double hi, int n, int o, double *plane, double *out) {
   int Ho = oracle_convT_out_size(H, k, stride, pad), Wo = oracle_convT_out_size(W, k, stride, pad);
-  for (int h = 0; h < Ho; ++h)
-    for (int ww = 0; ww < Wo; ++ww)
-      plane[(size_t)h * Wo + ww] =
-          convT2d_gather_at(x, w, b, C_in, H, W, C_out, k, stride, pad, n, o, h, ww);
+  convT2d_plane(x, w, b, C_in, H, W, C_out, k, stride, pad, n, o, plane);
   *out = oracle_pool_htanh_mean_tanh_plane(plane, Ho, Wo, pk, ps, lo, hi);
+  return ORACLE_OK;
+}
+
+/* The transposed conv's output planes as the model path computes them
+ * (convT2d_plane), z[N][C_out][Ho][Wo]: lets the tests compare that path with
+ * the gather and scatter forms directly. */
+int oracle_convT2d_planes(const float *x, const float *w, const float *b, double *z, int N,
+                          int C_in, int H, int W, int C_out, int k, int stride, int pad) {
+  if (!x || !w || !z || N < 1 || C_in < 1 || C_out < 1 || k < 1 || stride < 1 || pad < 0)
+    return ORACLE_EBADARG;
+  int Ho = oracle_convT_out_size(H, k, stride, pad), Wo = oracle_convT_out_size(W, k, stride, pad);
+  if (Ho < 1 || Wo < 1) return ORACLE_EBADARG;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int o = 0; o < C_out; ++o)
+      convT2d_plane(x, w, b, C_in, H, W, C_out, k, stride, pad, n, o,
+                    z + ((size_t)n * C_out + o) * Ho * Wo);
   return ORACLE_OK;
 }
 
@@ -438,28 +481,27 @@ int oracle_pool_htanh_mean_tanh(const double *z, double *y, int N, int C, int H,
   return ORACLE_OK;
 }
 
-/* Same tail reading fp32 input (what the GPU operator consumes). */
+/* Same tail reading fp32 input (what the GPU operator consumes): each plane
+ * is widened to double in the caller's scratch (room for (number of threads)
+ * * H * W doubles) and goes through the plane function above. */
 int oracle_pool_htanh_mean_tanh_f32(const float *z, double *y, int N, int C, int H, int W, int pk,
-                                    int ps, double lo, double hi) {
-  if (!z || !y || N < 1 || C < 1 || H < 1 || W < 1 || pk < 1 || ps < 1) return ORACLE_EBADARG;
+                                    int ps, double lo, double hi, double *scratch,
+                                    int64_t scratch_doubles) {
+  if (!z || !y || !scratch || N < 1 || C < 1 || H < 1 || W < 1 || pk < 1 || ps < 1)
+    return ORACLE_EBADARG;
   if (oracle_pool_out_size(H, pk, ps) < 1 || oracle_pool_out_size(W, pk, ps) < 1) return ORACLE_EBADARG;
-  int PH = oracle_pool_out_size(H, pk, ps), PW = oracle_pool_out_size(W, pk, ps);
+  if (scratch_doubles < (int64_t)oracle_num_threads() * H * W) return ORACLE_EBADARG;
 #pragma omp parallel for collapse(2) schedule(static)
   for (int n = 0; n < N; ++n)
     for (int c = 0; c < C; ++c) {
+      int t = 0;
+#ifdef _OPENMP
+      t = omp_get_thread_num();
+#endif
+      double *plane = scratch + (size_t)t * H * W;
       const float *zp = z + ((size_t)n * C + c) * H * W;
-      double sum = 0.0;
-      for (int ph = 0; ph < PH; ++ph)
-        for (int pw = 0; pw < PW; ++pw) {
-          double m = zp[(size_t)(ph * ps) * W + (pw * ps)];
-          for (int dh = 0; dh < pk; ++dh)
-            for (int dw = 0; dw < pk; ++dw) {
-              double v = zp[(size_t)(ph * ps + dh) * W + (pw * ps + dw)];
-              if (v > m) m = v;
-            }
-          sum += oracle_clamp(m, lo, hi);
-        }
-      y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)PW));
+      for (size_t p = 0; p < (size_t)H * W; ++p) plane[p] = (double)zp[p];
+      y[(size_t)n * C + c] = oracle_pool_htanh_mean_tanh_plane(plane, H, W, pk, ps, lo, hi);
     }
   return ORACLE_OK;
 }

@@ -100,3 +100,56 @@ def test_bench_refuses_more_than_one_gpu():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+@pytest.mark.parametrize("op,sizes", [
+    ("conv2d_relu_hswish", dict(N=3, C_in=8, H=12, W=10, C_out=64, k=3)),
+    ("conv3d_lrelu_add_clamp_gelu", dict(N=9, C_in=8, D=4, H=6, W=5, C_out=16, k=3, slope=0.2, lo=-1.0, hi=1.0)),
+    ("convT2d_pool_htanh_mean_tanh", dict(N=2, C_in=8, H=6, W=8, C_out=16, k=3, stride=1, pad=1, pool_k=2,
+                                          pool_s=2, lo=-1.0, hi=1.0)),
+    ("pool_htanh_mean_tanh", dict(N=2, C=3, H=6, W=8, pool_k=2, pool_s=2, lo=-1.0, hi=1.0)),
+    ("lrelu_add_clamp_gelu", dict(N=9, C=3, D=2, H=3, W=4, slope=0.2, lo=-1.0, hi=1.0)),
+])
+def test_oracle_check_counts_every_output_and_flags_errors(op, sizes):
+    """The bench's oracle leg compares every output (in chunks of images) and
+    counts those outside the tolerance: the oracle's own result passes, and
+    one planted error is found."""
+    import numpy as np
+    import oracle as O
+    from conv_inputs import make_inputs
+    shape = dict(op=op, **sizes)
+    keys = ("N", "C_in", "H", "W", "C_out", "k", "D", "C")
+    p = make_inputs(op, 4, **{k: v for k, v in sizes.items() if k in keys})
+    if op == "conv2d_relu_hswish":
+        ref = O.conv2d_relu_hswish(p["x"], p["w"], p["b"])
+    elif op == "conv3d_lrelu_add_clamp_gelu":
+        ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"])
+    elif op == "convT2d_pool_htanh_mean_tanh":
+        ref = O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], p["b"])[:, :, None, None]
+    elif op == "pool_htanh_mean_tanh":
+        ref = O.pool_htanh_mean_tanh(p["z"])[:, :, None, None]
+    else:
+        ref = O.lrelu_add_clamp_gelu_array(p["z"], p["s"])
+    gpu = ref.astype(np.float32)
+    base, err = bench.oracle_check("tiny", shape, p, gpu)
+    assert err["outputs"] == ref.size and err["over_tolerance"] == 0 and err["finite"]
+    assert base["kind"] == "oracle" and base["cores"] >= 1 and base["value"] > 0
+    assert base["sample"].startswith("every output")
+    bad = gpu.copy()
+    bad.reshape(-1)[ref.size - 1] += 1e-2
+    _, err = bench.oracle_check("tiny", shape, p, bad)
+    assert err["over_tolerance"] == 1 and err["max_abs"] >= 9e-3
+
+
+def test_oracle_check_samples_convT_within_budget():
+    """Past its time budget the transposed-convolution check computes a
+    random subset of (image, channel) outputs and says so."""
+    import numpy as np
+    import oracle as O
+    from conv_inputs import make_inputs
+    sizes = dict(N=4, C_in=16, H=16, W=16, C_out=64, k=3, stride=1, pad=1, pool_k=2, pool_s=2, lo=-1.0, hi=1.0)
+    p = make_inputs("convT2d_pool_htanh_mean_tanh", 5, N=4, C_in=16, H=16, W=16, C_out=64, k=3)
+    gpu = O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], p["b"]).astype(np.float32)[:, :, None, None]
+    base, err = bench.oracle_check("tiny", dict(op="convT2d_pool_htanh_mean_tanh", **sizes), p, gpu, budget_s=1e-9)
+    assert err["outputs"] < 256 and err["over_tolerance"] == 0
+    assert "of 256 (image, channel) outputs" in base["sample"]

@@ -4,9 +4,11 @@ Bar: every element within |gpu - ref| <= 1e-4 + 1e-4 * |ref| (the fp32
 atol = rtol = 1e-4 tolerance of the l2_p90 problem statement), no NaN/Inf.
 Small cases compare every element and cover several tiles, ragged tails,
 odd sizes (scalar load/store paths), the minimum sizes and a NULL bias.
-Full-size workloads run in the launch configuration the benchmark times and
-are checked on sampled outputs the oracle computes one by one, plus
-properties that hold at any size (output range, determinism).
+Every full-size workload runs in the launch configuration the benchmark
+times and is compared with the oracle at every output (the N = 128
+transposed-convolution workload is also marked slow), plus properties that
+hold at any size (output range, determinism).  At the ABI's size limits the
+outputs are sampled and computed one by one by the oracle.
 """
 import math
 
@@ -105,16 +107,14 @@ def test_conv2d_workload_n8_full(cce):
     assert_close(y.cpu().numpy(), O.conv2d_relu_hswish(p["x"], p["w"], p["b"]), "conv2d n8 full")
 
 
-def test_conv2d_workload_n128_sampled(cce):
+def test_conv2d_workload_n128_full(cce):
     shape, p = workload_inputs("conv2d_relu_hswish_n128", seed=0)
     y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
     torch.cuda.synchronize()
     yh = y.cpu().numpy()
     assert yh.shape == (128, 64, 126, 126)
     assert np.all(np.isfinite(yh)) and yh.min() >= 0.0  # HardSwish(ReLU(.)) >= 0
-    idx = sample_indices(yh.size, 20000, 1)
-    ref = O.conv2d_relu_hswish_at(p["x"], p["w"], p["b"], idx)
-    assert_close(yh.reshape(-1)[idx], ref, "conv2d n128 sampled")
+    assert_close(yh, O.conv2d_relu_hswish(p["x"], p["w"], p["b"]), "conv2d n128 every output")
 
 
 # ---------------------------------------------------------------------------
@@ -186,19 +186,27 @@ def test_conv3d_other_epilogue_parameters(cce):
         assert_close(y.cpu().numpy(), ref, f"conv3d slope={slope} clamp=[{lo},{hi}]")
 
 
-def test_conv3d_workload_n128_sampled(cce):
+def test_conv3d_workload_n128_full(cce):
+    """Every one of the 440,860,672 outputs against the oracle, eight images
+    at a time (the oracle's double output for the whole batch would be 3.5 GB)."""
     shape, p = workload_inputs("conv3d_lrelu_add_clamp_gelu_n128", seed=0)
     y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]),
                                         shape["slope"], shape["lo"], shape["hi"])
     torch.cuda.synchronize()
     yh = y.cpu().numpy()
+    del y
     assert yh.shape == (128, 64, 14, 62, 62)
     assert np.all(np.isfinite(yh))
     assert yh.min() >= GELU_LO - 1e-6 and yh.max() <= GELU_HI + 1e-6
-    idx = sample_indices(yh.size, 20000, 2)
-    ref = O.conv3d_lrelu_add_clamp_gelu_at(p["x"], p["w"], p["b"], p["s"], idx, shape["slope"],
-                                           shape["lo"], shape["hi"])
-    assert_close(yh.reshape(-1)[idx], ref, "conv3d n128 sampled")
+    worst = 0.0
+    for n0 in range(0, 128, 8):
+        ref = O.conv3d_lrelu_add_clamp_gelu(np.ascontiguousarray(p["x"][n0:n0 + 8]), p["w"], p["b"], p["s"],
+                                            shape["slope"], shape["lo"], shape["hi"])
+        err = np.abs(yh[n0:n0 + 8].astype(np.float64) - ref)
+        bad = err > ATOL + RTOL * np.abs(ref)
+        assert not bad.any(), f"conv3d n128 images {n0}..{n0 + 7}: {int(bad.sum())} outputs outside tolerance"
+        worst = max(worst, float(err.max()))
+    print(f"conv3d n128 every output: max abs err {worst:.3e} over {yh.size} values", flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -247,11 +255,16 @@ def test_convT_other_layer_shapes(cce, C_in, C_out, N, H, W):
     assert_close(y.cpu().numpy()[:, :, 0, 0], ref, f"convT {C_in}->{C_out} N={N} {H}x{W}")
 
 
+def garbage_workspace(nbytes):
+    """A workspace whose every byte is 0xFF: no call may rely on its contents."""
+    return torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
+
+
 def test_convT_workspace_shared_between_layer_shapes(cce):
-    """One zeroed workspace serves calls of different channel counts in turn."""
+    """One workspace, never cleared, serves calls of different channel counts in turn."""
     shapes = [(64, 64, 3, 36, 40), (8, 16, 5, 22, 18), (32, 32, 2, 48, 20)]
     need = max(cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(N, ci, H, W, co) for ci, co, N, H, W in shapes)
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = garbage_workspace(need)
     ins = [make_inputs(CONVT, seed=900 + i, N=N, C_in=ci, H=H, W=W, C_out=co, k=3)
            for i, (ci, co, N, H, W) in enumerate(shapes)]
     for rep in range(2):
@@ -260,7 +273,26 @@ def test_convT_workspace_shared_between_layer_shapes(cce):
             torch.cuda.synchronize()
             assert_close(y.cpu().numpy()[:, :, 0, 0], O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], p["b"]),
                          f"convT shared workspace {ci}->{co} pass {rep}")
-    assert int(ws[:256].count_nonzero()) == 0, "per-image counters not reset"
+
+
+def test_convT_workspace_reused_by_more_images_than_before(cce):
+    """Regression: the per-image counters occupy N * 4 bytes (rounded up to
+    256) ahead of the prepared weight, so a call with more images than the
+    previous user of the workspace finds the previous call's weight where its
+    counters lie.  Each call zeroes its own counters first: N = 16 at 256 x 256
+    followed by N = 100 at 32 x 32 (and back) on one workspace both match the
+    oracle."""
+    cases = [(16, 256, 256), (100, 32, 32), (16, 256, 256), (100, 32, 32)]
+    need = max(cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(N, 64, H, W, 64) for N, H, W in cases)
+    ws = garbage_workspace(need)
+    refs = {}
+    for i, (N, H, W) in enumerate(cases):
+        p = make_inputs(CONVT, seed=1300 + N, N=N, C_in=64, H=H, W=W, C_out=64, k=3)
+        if (N, H, W) not in refs:
+            refs[(N, H, W)] = O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], p["b"])
+        y = cce.convT2d_pool_htanh_mean_tanh(dev(p["x"]), dev(p["w"]), dev(p["b"]), workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy()[:, :, 0, 0], refs[(N, H, W)], f"convT reused workspace call {i}: N={N} {H}x{W}")
 
 
 def test_convT_hardtanh_bounds_and_saturation(cce):
@@ -281,7 +313,7 @@ def test_convT_workspace_reuse_across_shapes_and_determinism(cce):
     x2, w2, b2 = dev(p2["x"]), dev(p2["w"]), dev(p2["b"])
     need = max(cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(4, 64, 48, 40, 64),
                cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(2, 64, 18, 70, 64))
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = garbage_workspace(need)
     outs1, outs2 = [], []
     for _ in range(3):
         outs1.append(cce.convT2d_pool_htanh_mean_tanh(x1, w1, b1, workspace=ws).cpu().numpy())
@@ -292,9 +324,6 @@ def test_convT_workspace_reuse_across_shapes_and_determinism(cce):
         assert np.array_equal(o, outs2[0]), "convT result not bitwise reproducible"
     assert_close(outs1[0][:, :, 0, 0], O.convT2d_pool_htanh_mean_tanh(p1["x"], p1["w"], p1["b"]), "convT reuse A")
     assert_close(outs2[0][:, :, 0, 0], O.convT2d_pool_htanh_mean_tanh(p2["x"], p2["w"], p2["b"]), "convT reuse B")
-    # the kernel leaves the per-image counters at zero
-    torch.cuda.synchronize()
-    assert int(ws[:16].sum().item()) == 0
 
 
 def test_conv3d_alternating_tile_sizes(cce):
@@ -328,7 +357,7 @@ def test_calls_on_two_streams_at_once(cce):
     x3, w3, b3, s3 = dev(p3["x"]), dev(p3["w"]), dev(p3["b"]), dev(p3["s"])
     xt = [(dev(p["x"]), dev(p["w"]), dev(p["b"])) for p in pt]
     need = cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(2, 64, 32, 34, 64)
-    wss = [torch.zeros(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    wss = [garbage_workspace(need) for _ in range(2)]
 
     def run_a():
         return (cce.conv2d_relu_hswish(x2, w2, b2),
@@ -358,23 +387,33 @@ def test_calls_on_two_streams_at_once(cce):
         torch.cuda.synchronize()
         for got, want, what in zip(a + b, serial, ("conv2d", "convT 0", "conv3d", "convT 1")):
             assert np.array_equal(got.cpu().numpy(), want), f"two streams, pass {rep}: {what} differs from serial"
-    assert all(int(ws[:256].count_nonzero()) == 0 for ws in wss), "per-image counters not reset"
 
 
-@pytest.mark.parametrize("name,count", [("convT2d_pool_htanh_mean_tanh_n16", 48),
-                                        ("convT2d_pool_htanh_mean_tanh_n128", 32)])
-def test_convT_workload_sampled(cce, name, count):
+def check_convT_workload_full(cce, name):
+    """Every output of a full-size workload against the oracle, in the launch
+    configuration the benchmark times, plus bitwise determinism and range."""
     shape, p = workload_inputs(name, seed=0)
-    y = cce.convT2d_pool_htanh_mean_tanh(dev(p["x"]), dev(p["w"]), dev(p["b"]))
-    y2 = cce.convT2d_pool_htanh_mean_tanh(dev(p["x"]), dev(p["w"]), dev(p["b"]))
+    x, w, b = dev(p["x"]), dev(p["w"]), dev(p["b"])
+    need = cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(shape["N"], 64, 256, 256, 64)
+    ws = garbage_workspace(need)
+    y = cce.convT2d_pool_htanh_mean_tanh(x, w, b, workspace=ws)
+    y2 = cce.convT2d_pool_htanh_mean_tanh(x, w, b, workspace=ws)
     torch.cuda.synchronize()
     yh = y.cpu().numpy()[:, :, 0, 0]
-    assert np.array_equal(yh, y2.cpu().numpy()[:, :, 0, 0])
+    assert np.array_equal(yh, y2.cpu().numpy()[:, :, 0, 0]), "not bitwise reproducible"
     assert np.all(np.abs(yh) <= math.tanh(1.0) + 1e-6)
-    rng = np.random.default_rng(3)
-    idx = np.unique(np.concatenate([rng.integers(0, yh.size, count), [0, yh.size - 1]]))
-    ref = O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], idx)
-    assert_close(yh.reshape(-1)[idx], ref, f"{name} sampled")
+    del x, w, b, y, y2, ws
+    ref = O.convT2d_pool_htanh_mean_tanh(p["x"], p["w"], p["b"])
+    assert_close(yh, ref, f"{name} every output")
+
+
+def test_convT_workload_n16_full(cce):
+    check_convT_workload_full(cce, "convT2d_pool_htanh_mean_tanh_n16")
+
+
+@pytest.mark.slow
+def test_convT_workload_n128_full(cce):
+    check_convT_workload_full(cce, "convT2d_pool_htanh_mean_tanh_n128")
 
 
 # ---------------------------------------------------------------------------
@@ -459,21 +498,22 @@ def test_elementwise_tail_in_place(cce, S):
     assert torch.equal(zz, ref)
 
 
-def test_elementwise_tail_workload_sampled(cce):
+def test_elementwise_tail_workload_full(cce):
+    """Every element of the [128, 64, 14, 62, 62] workload, eight images at a time."""
     shape, p = workload_inputs("lrelu_add_clamp_gelu_n128", seed=0)
     y = cce.lrelu_add_clamp_gelu(dev(p["z"]), dev(p["s"]), shape["slope"], shape["lo"], shape["hi"])
     torch.cuda.synchronize()
     yh = y.cpu().numpy()
+    del y
     assert np.all(np.isfinite(yh)) and yh.min() >= GELU_LO - 1e-6 and yh.max() <= GELU_HI + 1e-6
-    # whole planes at the two ends plus random elements
-    idx = sample_indices(yh.size, 200000, 5)
-    zf = p["z"].reshape(-1)
-    C, S = shape["C"], yh.size // (shape["N"] * shape["C"])
-    ch = (idx // S) % C
-    ref = np.array([O.lrelu_add_clamp_gelu(zf[i], p["s"][c]) for i, c in zip(idx[:20000], ch[:20000])])
-    assert_close(yh.reshape(-1)[idx[:20000]], ref, "elementwise tail n128 sampled")
-    head = O.lrelu_add_clamp_gelu_array(p["z"][:1], p["s"])
-    assert_close(yh[:1], head, "elementwise tail n128 first image")
+    worst = 0.0
+    for n0 in range(0, shape["N"], 8):
+        ref = O.lrelu_add_clamp_gelu_array(p["z"][n0:n0 + 8], p["s"], shape["slope"], shape["lo"], shape["hi"])
+        err = np.abs(yh[n0:n0 + 8].astype(np.float64) - ref)
+        bad = err > ATOL + RTOL * np.abs(ref)
+        assert not bad.any(), f"elementwise tail images {n0}..{n0 + 7}: {int(bad.sum())} outside tolerance"
+        worst = max(worst, float(err.max()))
+    print(f"elementwise tail n128 every element: max abs err {worst:.3e} over {yh.size} values", flush=True)
 
 
 # ---------------------------------------------------------------------------

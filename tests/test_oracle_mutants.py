@@ -58,11 +58,9 @@ MUTANTS = {
                           "      sum += m; (void)lo; (void)hi;\n    }\n  return tanh")],
     "mean_divisor": [("return tanh(sum / ((double)PH * (double)PW));",
                       "return tanh(sum / ((double)PH * (double)PW + 1.0));")],
-    "f32_tail_hardtanh_dropped": [("          sum += oracle_clamp(m, lo, hi);\n        }\n      y[",
-                                   "          sum += m; (void)lo; (void)hi;\n        }\n      y[")],
-    "f32_tail_window_row_offset": [(
-        "double v = zp[(size_t)(ph * ps + dh) * W + (pw * ps + dw)];",
-        "double v = zp[(size_t)(ph * ps + dw) * W + (pw * ps + dw)];")],
+    "f32_tail_widened_off_by_one": [(
+        "for (size_t p = 0; p < (size_t)H * W; ++p) plane[p] = (double)zp[p];",
+        "for (size_t p = 0; p < (size_t)H * W; ++p) plane[p] = (double)zp[p + (p + 1 < (size_t)H * W)];")],
     "f32_elementwise_channel_of_s": [("(double)z[base + e], (double)s[c]",
                                       "(double)z[base + e], (double)s[(c + 1) % C]")],
     "conv3d_model_channel_of_s": [(
@@ -94,8 +92,15 @@ MUTANTS = {
         "int ww) {\n  double acc = 0.0; (void)b;\n  for (int i = 0; i < C_in; ++i)\n    for (int kh = 0; kh < k; ++kh) {\n      int th")],
     "convT_scatter_flipped_positions": [("int oh = ih * stride - pad + kh, ow = iw * stride - pad + kw;",
                                          "int oh = ih * stride + pad - kh, ow = iw * stride + pad - kw;")],
-    "f32_tail_mean_divisor": [("y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)PW));",
-                               "y[(size_t)n * C + c] = tanh(sum / ((double)PH * (double)(PW + 1)));")],
+    "convT_model_plane_flipped_positions": [("int oh = ih * stride - pad + kh;", "int oh = ih * stride + pad - kh;"),
+                                            ("int ow = iw * stride - pad + kw;", "int ow = iw * stride + pad - kw;")],
+    "convT_model_plane_bias_dropped": [("for (size_t p = 0; p < (size_t)Ho * Wo; ++p) z[p] = bias_of(b, o);",
+                                       "for (size_t p = 0; p < (size_t)Ho * Wo; ++p) z[p] = 0.0; (void)b;")],
+    "convT_model_plane_weight_as_c_out_by_c_in": [(
+        "double wv = (double)w[(((size_t)i * C_out + o) * k + kh) * k + kw];",
+        "double wv = (double)w[(((size_t)o * C_in + i) * k + kh) * k + kw];")],
+    "convT_model_plane_input_channel": [("const float *xp = x + ((size_t)n * C_in + i) * H * W;",
+                                        "const float *xp = x + ((size_t)n * C_in + (i + 1) % C_in) * H * W;")],
 }
 
 

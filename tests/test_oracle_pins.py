@@ -328,6 +328,9 @@ def test_convT_scatter_equals_gather_and_torch(case):
     ref = F.conv_transpose2d(_t64(x), _t64(w), _t64(b), stride=s, padding=p).numpy()
     assert ref.shape == zs.shape
     np.testing.assert_allclose(zs, ref, rtol=0, atol=1e-12)
+    # The model path's tap-major scatter adds each output's terms in the
+    # gather form's (i, kh, kw) order: the same doubles, bit for bit.
+    np.testing.assert_array_equal(O.convT2d_planes(x, w, b, s, p), zg)
 
 
 def test_convT_adjoint_identity():
@@ -340,9 +343,10 @@ def test_convT_adjoint_identity():
     y = O.convT2d_gather(x, w, None, 1, p)
     z = _rand(rng, *y.shape)
     zp = np.ascontiguousarray(np.pad(z, ((0, 0), (0, 0), (p, p), (p, p))))
-    lhs = float(np.sum(y * z.astype(np.float64)))
     rhs = float(np.sum(x.astype(np.float64) * O.conv2d(zp, w, None)))
-    assert lhs == pytest.approx(rhs, rel=1e-12, abs=1e-12)
+    for yy in (y, O.convT2d_planes(x, w, None, 1, p)):
+        lhs = float(np.sum(yy * z.astype(np.float64)))
+        assert lhs == pytest.approx(rhs, rel=1e-12, abs=1e-12)
 
 
 def test_convT_impulse_stamps_unflipped_kernel():
@@ -352,7 +356,8 @@ def test_convT_impulse_stamps_unflipped_kernel():
     x = np.zeros((1, C_in, H, W), np.float32)
     h0, w0 = 2, 4
     x[0, 1, h0, w0] = 1.0
-    for z in (O.convT2d_scatter(x, w, None, 1, 1)[0], O.convT2d_gather(x, w, None, 1, 1)[0]):
+    for z in (O.convT2d_scatter(x, w, None, 1, 1)[0], O.convT2d_gather(x, w, None, 1, 1)[0],
+              O.convT2d_planes(x, w, None, 1, 1)[0]):
         expect = np.zeros_like(z)
         expect[:, h0 - 1:h0 + 2, w0 - 1:w0 + 2] = w[1]
         np.testing.assert_array_equal(z, expect)
