@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     conv2d_relu_hswish,
     conv3d_lrelu_add_clamp_gelu,
     convT2d_pool_htanh_mean_tanh,
+    convT2d_pool_htanh_mean_tanh_noalloc,
     convT2d_pool_htanh_mean_tanh_workspace_bytes,
     library_path,
     lrelu_add_clamp_gelu,

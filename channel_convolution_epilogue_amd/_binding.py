@@ -15,6 +15,7 @@ EXPORTED_SYMBOLS = (
     "conv2d_relu_hswish",
     "conv3d_lrelu_add_clamp_gelu",
     "convT2d_pool_htanh_mean_tanh",
+    "convT2d_pool_htanh_mean_tanh_noalloc",
     "convT2d_pool_htanh_mean_tanh_workspace_bytes",
     "lrelu_add_clamp_gelu",
     "pool_htanh_mean_tanh",
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
         L.conv3d_lrelu_add_clamp_gelu.argtypes = [fp] * 5 + [i] * 7 + [f] * 3 + [vp]
         L.convT2d_pool_htanh_mean_tanh.restype = i
         L.convT2d_pool_htanh_mean_tanh.argtypes = [fp] * 4 + [i] * 10 + [f, f, vp, sz, vp]
+        L.convT2d_pool_htanh_mean_tanh_noalloc.restype = i
+        L.convT2d_pool_htanh_mean_tanh_noalloc.argtypes = [fp] * 4 + [i] * 10 + [f, f, vp]
         L.convT2d_pool_htanh_mean_tanh_workspace_bytes.restype = sz
         L.convT2d_pool_htanh_mean_tanh_workspace_bytes.argtypes = [i] * 10
         L.pool_htanh_mean_tanh.restype = i
@@ -243,6 +246,32 @@ def convT2d_pool_htanh_mean_tanh(x, w, b=None, stride=1, padding=1, pool_k=2, po
                                             padding, pool_k, pool_s, float(htanh_lo), float(htanh_hi),
                                             workspace.data_ptr(), ws_bytes, stream)
     _check("convT2d_pool_htanh_mean_tanh", st)
+    return out
+
+
+def convT2d_pool_htanh_mean_tanh_noalloc(x, w, b=None, stride=1, padding=1, pool_k=2, pool_s=2,
+                                         htanh_lo=-1.0, htanh_hi=1.0, out=None):
+    """convT2d_pool_htanh_mean_tanh on the library's static per-device scratch
+    instead of a workspace: the C call allocates nothing (pass `out` to keep
+    this wrapper from allocating the result).  Calls that overlap in time on
+    one GPU race on that scratch."""
+    import torch
+    L = load()
+    _dims(x, 4, "x")
+    _dims(w, 4, "w")
+    N, C_in, H, W = x.shape
+    _, C_out, k, _ = w.shape
+    _expect(w, (C_in, C_out, k, k), "w")
+    _expect(b, (C_out,), "b")
+    _expect(out, (N, C_out, 1, 1), "out")
+    _same_device(x, w=w, b=b, out=out)
+    if out is None:
+        out = torch.empty((N, C_out, 1, 1), device=x.device, dtype=torch.float32)
+    with _on_device(x):
+        st = L.convT2d_pool_htanh_mean_tanh_noalloc(
+            _dev_ptr(x, "x", 4), _dev_ptr(w, "w", 4), _dev_ptr(b, "b", 1), _dev_ptr(out, "out", 4), N, C_in,
+            H, W, C_out, k, stride, padding, pool_k, pool_s, float(htanh_lo), float(htanh_hi), _stream(x))
+    _check("convT2d_pool_htanh_mean_tanh_noalloc", st)
     return out
 
 

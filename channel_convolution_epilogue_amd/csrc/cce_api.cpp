@@ -64,6 +64,8 @@ const char *cce_status_string(int status) {
     case CCE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case CCE_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case CCE_ERR_TOO_LARGE: return "problem too large for 32-bit index arithmetic";
+    case CCE_ERR_SCRATCH_LIMIT:
+      return "the call needs more than the library's static scratch (CCE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -148,6 +150,19 @@ int convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b,
     return CCE_ERR_WORKSPACE;
   return cce::launch_convT2d_pool_htanh_mean_tanh(x, w, b, y, N, C_in, H, W, C_out, htanh_lo,
                                                   htanh_hi, workspace, (hipStream_t)stream);
+}
+
+int convT2d_pool_htanh_mean_tanh_noalloc(const float *x, const float *w, const float *b, float *y,
+                                         int N, int C_in, int H, int W, int C_out, int k, int stride,
+                                         int pad, int pool_k, int pool_s, float htanh_lo,
+                                         float htanh_hi, void *stream) {
+  if (!x || !w || !y) return CCE_ERR_NULL;
+  const int st = convT_check_shape(N, C_in, H, W, C_out, k, stride, pad, pool_k, pool_s);
+  if (st != CCE_OK) return st;
+  if (!is_finite_f(htanh_lo) || !is_finite_f(htanh_hi) || htanh_lo > htanh_hi) return CCE_ERR_UNSUPPORTED;
+  if (!aligned4(x) || !aligned4(w) || !aligned4(y) || (b && !aligned4(b))) return CCE_ERR_ALIGN;
+  return cce::launch_convT2d_pool_htanh_mean_tanh_noalloc(x, w, b, y, N, C_in, H, W, C_out, htanh_lo,
+                                                          htanh_hi, (hipStream_t)stream);
 }
 
 int pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, int pool_k,

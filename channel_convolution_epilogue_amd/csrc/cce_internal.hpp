@@ -44,6 +44,11 @@ size_t convT_workspace_bytes(int N, int C_in, int H, int W, int C_out);
 int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b, float *y,
                                         int N, int C_in, int H, int W, int C_out, float lo, float hi,
                                         void *workspace, hipStream_t stream);
+// The same with the library's static per-device scratch as the workspace
+// (CCE_ERR_SCRATCH_LIMIT when the call needs more than it holds).
+int launch_convT2d_pool_htanh_mean_tanh_noalloc(const float *x, const float *w, const float *b,
+                                                float *y, int N, int C_in, int H, int W, int C_out,
+                                                float lo, float hi, hipStream_t stream);
 
 // Epilogue-only operators over a precomputed convolution output.
 int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, int W, int pool_k,

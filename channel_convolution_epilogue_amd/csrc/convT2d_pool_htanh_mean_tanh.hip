@@ -33,6 +33,14 @@
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
 
+// Scratch of convT2d_pool_htanh_mean_tanh_noalloc, the entry point for
+// callers that cannot allocate device memory: what the workspace holds for
+// the other entry point (counters, prepared weight, partial sums), in a
+// file-scope device array.  Each GPU the library runs on holds its own copy
+// until the process ends; host code uses the per-device address that
+// hipGetSymbolAddress returns, never this name.
+static __device__ __align__(256) unsigned char scratch[CCE_NOALLOC_SCRATCH_BYTES];
+
 namespace cce {
 namespace {
 
@@ -405,6 +413,28 @@ int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const fl
       if (C_in == 64) return launch_for<OutCh<64>, 64 / CC>(a, w, wprep, N, grid, stream);
       return launch_for<OutCh<64>, 0>(a, w, wprep, N, grid, stream);
   }
+}
+
+namespace {
+// Device address of `scratch`, per device (null until the first call there).
+std::atomic<void *> g_scratch[kLaunchCacheDevices];
+}  // namespace
+
+int launch_convT2d_pool_htanh_mean_tanh_noalloc(const float *x, const float *w, const float *b,
+                                                float *y, int N, int C_in, int H, int W, int C_out,
+                                                float lo, float hi, hipStream_t stream) {
+  if (convT_workspace_bytes(N, C_in, H, W, C_out) > (size_t)CCE_NOALLOC_SCRATCH_BYTES)
+    return CCE_ERR_SCRATCH_LIMIT;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CCE_ERR_LAUNCH;
+  const bool cached = dev >= 0 && dev < kLaunchCacheDevices;
+  void *ptr = cached ? g_scratch[dev].load(std::memory_order_acquire) : nullptr;
+  if (!ptr) {
+    // Once per device, with that device current: the array's address on it.
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return CCE_ERR_LAUNCH;
+    if (cached) g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  return launch_convT2d_pool_htanh_mean_tanh(x, w, b, y, N, C_in, H, W, C_out, lo, hi, ptr, stream);
 }
 
 }  // namespace cce

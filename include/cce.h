@@ -55,7 +55,8 @@ typedef enum {
   CCE_ERR_ALIGN = -4,       /* a tensor pointer is not 4-byte aligned */
   CCE_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or smaller than required */
   CCE_ERR_LAUNCH = -6,      /* the HIP runtime rejected the launch (no device, wrong arch ...) */
-  CCE_ERR_TOO_LARGE = -7    /* an index would overflow the kernels' 32-bit arithmetic */
+  CCE_ERR_TOO_LARGE = -7,   /* an index would overflow the kernels' 32-bit arithmetic */
+  CCE_ERR_SCRATCH_LIMIT = -8 /* the call needs more than the static scratch of the _noalloc entry */
 } cce_status;
 
 /* Human-readable text for a cce_status value (static storage, never NULL). */
@@ -155,6 +156,33 @@ int convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const float *b,
 size_t convT2d_pool_htanh_mean_tanh_workspace_bytes(int N, int C_in, int H, int W, int C_out,
                                                     int k, int stride, int pad, int pool_k,
                                                     int pool_s);
+
+/* Size of the static per-device scratch behind the _noalloc entry point. */
+#define CCE_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * convT2d_pool_htanh_mean_tanh without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results, bit for bit, and errors as convT2d_pool_htanh_mean_tanh, whose
+ * kernels it runs.
+ *
+ * In place of the workspace it uses a file-scope device array of
+ * CCE_NOALLOC_SCRATCH_BYTES (8 MiB) that each GPU the library runs on holds
+ * from its first call until the process ends; the first call on a device
+ * looks up that device's copy (hipGetSymbolAddress) and caches its address.
+ * The call allocates and frees nothing and issues no memset.  A call whose
+ * workspace_bytes(...) would exceed the scratch returns
+ * CCE_ERR_SCRATCH_LIMIT and launches nothing (the page's layer, 64 -> 64 at
+ * 256 x 256, fits up to N = 251).  All calls on one GPU share its scratch:
+ * calls that overlap in time on that GPU (on different streams or threads)
+ * race and give wrong results; calls on one stream, or otherwise ordered,
+ * are safe.
+ */
+int convT2d_pool_htanh_mean_tanh_noalloc(const float *x, const float *w, const float *b, float *y,
+                                         int N, int C_in, int H, int W, int C_out, int k, int stride,
+                                         int pad, int pool_k, int pool_s, float htanh_lo,
+                                         float htanh_hi, void *stream);
 
 /*
  * Epilogue-only operators over a precomputed convolution output (the

@@ -15,13 +15,14 @@ import channel_convolution_epilogue_amd as cce
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "cce.h"
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, ELAUNCH, ETOOBIG = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, ELAUNCH, ETOOBIG, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 FAKE = 0x10000  # a non-NULL, 16-byte aligned address that is never dereferenced
 
 
 def declared_functions():
     text = HEADER.read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)  # preprocessor lines (macro constants)
     return sorted(set(re.findall(r"\b([a-zA-Z_][a-zA-Z0-9_]*)\s*\(", text)) -
                   {"if", "defined", "sizeof"})
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, ELAUNCH, ETOOBIG):
+    for st in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, ELAUNCH, ETOOBIG, ESCRATCH):
         s = cce.status_string(st)
         assert s and s != "unknown status"
     assert cce.status_string(12345) == "unknown status"
@@ -119,6 +120,25 @@ def test_convT_validation(lib):
     need = cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(2, 64, 16, 16, 64)
     assert ct(lib, ws_bytes=need - 1) == EWS
     assert ct(lib, N=1 << 12, H=1024, W=1024) == ETOOBIG
+
+
+def test_convT_noalloc_validation(lib):
+    """The entry point without a workspace validates like the one with it, and
+    rejects calls whose workspace would not fit its static 8 MiB scratch
+    before any HIP call: the page's layer at 256 x 256 fits up to N = 251."""
+    def nt(N=2, H=16, W=16, C_in=64, C_out=64, x=FAKE, y=FAKE, stride=1, lo=-1.0, hi=1.0):
+        return lib.convT2d_pool_htanh_mean_tanh_noalloc(x, FAKE, None, y, N, C_in, H, W, C_out, 3, stride, 1,
+                                                        2, 2, lo, hi, None)
+    assert nt(x=None) == ENULL
+    assert nt(H=1) == ESHAPE
+    assert nt(stride=2) == EUNSUP
+    assert nt(C_out=48) == EUNSUP
+    assert nt(lo=2.0, hi=1.0) == EUNSUP
+    assert nt(y=FAKE + 2) == EALIGN
+    assert nt(N=252, H=256, W=256) == ESCRATCH
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(251, 64, 256, 256, 64) <= 8 << 20
+    assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(252, 64, 256, 256, 64) > 8 << 20
+    assert "scratch" in cce.status_string(ESCRATCH)
 
 
 def test_convT_workspace_size(lib):
