@@ -660,6 +660,8 @@ def main():
                          "hbm_frac": r["hbm_frac"], "hot": r["hot"]}
             if "cold" in r:
                 ops[name]["cold"] = r["cold"]
+            if "oracle" in r:
+                ops[name]["oracle"], ops[name]["gpu_error_vs_oracle"] = r["oracle"], r["gpu_error_vs_oracle"]
             if name in PAGES_ESTIMATE:
                 ops[name]["pages_estimate"] = PAGES_ESTIMATE[name]
     # The headline's oracle run last: the GPU is idle meanwhile, and the other

@@ -84,10 +84,55 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
     return LIB
 
 
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized_api(outdir: Path) -> Path:
+    """A debugging copy of the library whose C-ABI layer (cce_api.cpp: every
+    argument check, before any HIP call) is built with clang's
+    AddressSanitizer and UndefinedBehaviorSanitizer for the host code only,
+    linked with the regular kernel objects (built first if missing).  Load it
+    with the sanitizer runtime preloaded (sanitizer_runtime()); it never goes
+    to a GPU."""
+    outdir = Path(outdir)
+    outdir.mkdir(parents=True, exist_ok=True)
+    objdir = PKG / "_build"
+    kernels = [objdir / (Path(s).stem + ".o") for s in SOURCES if s != "cce_api.cpp"]
+    if not all(o.exists() for o in kernels):
+        build()
+    api = outdir / "cce_api_sanitized.o"
+    flags = [f"--offload-arch={ARCH}", "-O1", "-std=c++17", "-fPIC", "-Wall", "-I", str(INCLUDE),
+             "-I", str(CSRC), *SANITIZE]
+    _run([hipcc(), *flags, "-c", "-x", "hip", str(CSRC / "cce_api.cpp"), "-o", str(api)], False)
+    lib = outdir / "libcce_sanitized.so"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan", *SANITIZE[:4],
+          "-o", str(lib), str(api), *[str(o) for o in kernels]], False)
+    return lib
+
+
+def sanitizer_runtime() -> str:
+    """clang's shared AddressSanitizer runtime (which carries the
+    UndefinedBehaviorSanitizer handlers) matching hipcc, for LD_PRELOAD."""
+    rocm = Path(os.environ.get("ROCM_PATH", "/opt/rocm"))
+    found = sorted(rocm.glob("llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under " + str(rocm / "llvm"))
+    return str(found[-1])
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--verbose", action="store_true", help="print per-kernel register/LDS usage")
+    ap.add_argument("--sanitize-host", metavar="DIR",
+                    help="instead, build DIR/libcce_sanitized.so: the C-ABI layer with host "
+                         "AddressSanitizer + UndefinedBehaviorSanitizer (load it with "
+                         "LD_PRELOAD of the printed runtime)")
     args = ap.parse_args()
+    if args.sanitize_host:
+        print(build_sanitized_api(Path(args.sanitize_host)))
+        print("runtime:", sanitizer_runtime())
+        return
     print(build(verbose=args.verbose))
 
 

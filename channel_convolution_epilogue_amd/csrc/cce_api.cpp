@@ -1,10 +1,12 @@
 // extern "C" entry points of libcce: argument validation (host only, before any
 // HIP call), then one kernel launch per call.  No allocation, no
-// synchronisation and no mutable global state beyond per-device caches of
-// device properties and of each kernel instance's launch set-up.
+// synchronisation (unless CCE_DEBUG is set) and no mutable global state beyond
+// per-device caches of device properties and of each kernel instance's launch
+// set-up.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <atomic>
 
@@ -47,6 +49,17 @@ int current_device_info(DeviceInfo *info) {
   return CCE_OK;
 }
 
+bool debug_sync() {
+  static std::atomic<int> state{-1};  // -1 = not read yet
+  int v = state.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char *e = getenv("CCE_DEBUG");
+    v = (e && e[0] && !(e[0] == '0' && e[1] == 0)) ? 1 : 0;
+    state.store(v, std::memory_order_relaxed);
+  }
+  return v != 0;
+}
+
 }  // namespace cce
 
 static bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
@@ -70,7 +83,7 @@ const char *cce_status_string(int status) {
   }
 }
 
-int cce_version(void) { return 103; }
+int cce_version(void) { return 104; }
 
 // Layer shapes the Conv2d kernel is instantiated for (see the header).
 static bool conv2d_layer_supported(int C_in, int C_out, int k) {

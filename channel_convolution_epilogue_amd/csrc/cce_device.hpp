@@ -117,16 +117,17 @@ __device__ __forceinline__ float clampf(float v, float lo, float hi) {
 //   GELU(t) = 0.5 t + u P(u),   u = t^2,
 // with P the degree-4 polynomial that minimises max |u (P(u) - R(u))| over
 // u in [0, 1], where R(u) = (GELU(t) - 0.5 t) / u = erf(t / sqrt 2) / (2 t)
-// is even in t.  The coefficients come from a weighted least-squares fit in
-// double precision iterated towards that minimax fit.  With the coefficients
-// rounded to fp32 the approximation errs by less than 2e-8 in GELU -- below
-// the fp32 rounding of the evaluation itself (about 1e-7).  Four FMAs where
-// the Maclaurin series of erf needs seven for the same accuracy.
+// is even in t.  The coefficients are that minimax fit (a linear programme
+// in double precision, channel_convolution_epilogue_amd/gelu_poly_fit.py)
+// rounded to fp32; so rounded, the approximation errs by less than 2e-8 in
+// GELU -- below the fp32 rounding of the evaluation itself (about 1e-7).
+// Four FMAs where the Maclaurin series of erf needs seven for the same
+// accuracy.
 __device__ __forceinline__ float gelu_small(float t) {
   const float u = t * t;
-  float r = 9.09766386e-05f;
-  r = fmaf(r, u, -0.00116171769f);
-  r = fmaf(r, u, 0.00996111706f);
+  float r = 9.09758819e-05f;
+  r = fmaf(r, u, -0.00116171606f);
+  r = fmaf(r, u, 0.00996111613f);
   r = fmaf(r, u, -0.0664877221f);
   r = fmaf(r, u, 0.398942083f);
   return fmaf(u, r, 0.5f * t);

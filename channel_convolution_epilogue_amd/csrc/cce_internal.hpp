@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdio.h>
 
 #include <atomic>
 
@@ -99,9 +100,23 @@ inline int launch_setup(const void *kern, LaunchCache &cache, int device, size_t
   return per_cu;
 }
 
-// Map the runtime's last error after a launch onto a cce_status.
-inline int launch_status() {
-  return hipGetLastError() == hipSuccess ? CCE_OK : CCE_ERR_LAUNCH;
+// True when the environment variable CCE_DEBUG was set to a non-empty value
+// other than "0" when the library first looked (read once per process).
+bool debug_sync();
+
+// Map the runtime's last error after a launch onto a cce_status.  Under
+// CCE_DEBUG every launch is also followed by a synchronisation of its
+// stream, so that a kernel that faults is reported by the call that
+// launched it (on stderr, naming `what`) and the call returns
+// CCE_ERR_LAUNCH.  That synchronisation makes calls blocking and is not
+// allowed under HIP graph capture: CCE_DEBUG is for debugging only.
+inline int launch_status(hipStream_t stream, const char *what) {
+  hipError_t e = hipGetLastError();
+  const bool debug = debug_sync();
+  if (e == hipSuccess && debug) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) return CCE_OK;
+  if (debug) fprintf(stderr, "libcce: %s: %s\n", what, hipGetErrorString(e));
+  return CCE_ERR_LAUNCH;
 }
 
 }  // namespace cce

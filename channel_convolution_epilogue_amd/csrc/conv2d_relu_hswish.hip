@@ -319,7 +319,7 @@ int launch_instance(const Conv2dArgs &a, hipStream_t stream) {
   if (grid > needed) grid = needed;
   grid = (grid + 7) & ~7;  // the XCD remap needs a multiple of 8; surplus waves exit
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds_bytes, stream, a);
-  return launch_status();
+  return launch_status(stream, "conv2d_relu_hswish_kernel");
 }
 
 // Strip decomposition of one layer shape and its launch: 16-byte window

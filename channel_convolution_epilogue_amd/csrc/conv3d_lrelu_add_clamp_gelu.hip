@@ -286,7 +286,7 @@ int launch_instance(const Conv3dArgs &a, size_t lds_bytes, const DeviceInfo &dev
   if (grid > a.nblocks) grid = a.nblocks;
   grid = (grid + 7) & ~7;  // the XCD remap needs a multiple of 8; surplus workgroups exit
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds_bytes, stream, a);
-  return launch_status();
+  return launch_status(stream, "conv3d_lrelu_add_clamp_gelu_kernel");
 }
 
 template <class L, bool VL, bool VS, bool FIXED64>

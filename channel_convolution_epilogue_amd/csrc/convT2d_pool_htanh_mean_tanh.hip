@@ -356,7 +356,7 @@ int launch_for(ConvTArgs a, const float *w, float *wprep, int N, long long grid,
   const int prep_items = total > N ? total : N;
   hipLaunchKernelGGL(convT_prepare_weight_kernel<OC>, dim3((prep_items + THREADS - 1) / THREADS),
                      dim3(THREADS), 0, stream, w, wprep, total, a.tickets, N);
-  if (launch_status() != CCE_OK) return CCE_ERR_LAUNCH;
+  if (launch_status(stream, "convT_prepare_weight_kernel") != CCE_OK) return CCE_ERR_LAUNCH;
   const bool vec = (a.W % 4 == 0) && ((uintptr_t)a.x % 16 == 0);
   if (vec)
     hipLaunchKernelGGL((convT2d_pool_htanh_mean_tanh_kernel<OC, true, NCH>), dim3((unsigned)grid),
@@ -364,7 +364,7 @@ int launch_for(ConvTArgs a, const float *w, float *wprep, int N, long long grid,
   else
     hipLaunchKernelGGL((convT2d_pool_htanh_mean_tanh_kernel<OC, false, NCH>), dim3((unsigned)grid),
                        dim3(THREADS), 0, stream, a);
-  return launch_status();
+  return launch_status(stream, "convT2d_pool_htanh_mean_tanh_kernel");
 }
 
 }  // namespace

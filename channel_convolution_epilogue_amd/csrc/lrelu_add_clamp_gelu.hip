@@ -100,7 +100,7 @@ int launch_lrelu_add_clamp_gelu(const float *z, const float *s, float *y, int N,
       hipLaunchKernelGGL(lrelu_add_clamp_gelu_flat_kernel<true>, dim3(grid), dim3(FLAT_THREADS), 0, stream, a);
     else
       hipLaunchKernelGGL(lrelu_add_clamp_gelu_flat_kernel<false>, dim3(grid), dim3(FLAT_THREADS), 0, stream, a);
-    return launch_status();
+    return launch_status(stream, "lrelu_add_clamp_gelu_flat_kernel");
   }
   const long long chunks = (S + CHUNK - 1) / CHUNK;
   const long long grid = (long long)N * C * chunks;
@@ -111,7 +111,7 @@ int launch_lrelu_add_clamp_gelu(const float *z, const float *s, float *y, int N,
     hipLaunchKernelGGL(lrelu_add_clamp_gelu_kernel<true>, dim3((unsigned)grid), dim3(THREADS), 0, stream, a);
   else
     hipLaunchKernelGGL(lrelu_add_clamp_gelu_kernel<false>, dim3((unsigned)grid), dim3(THREADS), 0, stream, a);
-  return launch_status();
+  return launch_status(stream, "lrelu_add_clamp_gelu_kernel");
 }
 
 }  // namespace cce

@@ -138,7 +138,7 @@ int launch_pool_htanh_mean_tanh(const float *z, float *y, int N, int C, int H, i
   else
     hipLaunchKernelGGL(pool_htanh_mean_tanh_kernel<kGeneral>, dim3((unsigned)planes), dim3(THREADS), 0,
                        stream, a);
-  return launch_status();
+  return launch_status(stream, "pool_htanh_mean_tanh_kernel");
 }
 
 }  // namespace cce

@@ -65,7 +65,14 @@ const char *cce_status_string(int status);
 /* Library ABI version: 100 * major + minor (1.1: further layer shapes for
  * Conv2d and Conv3d, any pooling window and stride for the pooled tail;
  * 1.2: further channel counts for the fused ConvTranspose2d; 1.3: 1 x 1 x 1
- * Conv3d). */
+ * Conv3d; 1.4: convT2d_pool_htanh_mean_tanh_noalloc, and the transposed
+ * conv's workspace needs no initial contents).
+ *
+ * Debugging: with the environment variable CCE_DEBUG set (to anything but
+ * "" or "0") when the library is first used, every launch is followed by a
+ * synchronisation of its stream; a kernel that faults is then reported on
+ * stderr by the call that launched it, which returns CCE_ERR_LAUNCH.  Calls
+ * become blocking, and must not be captured into HIP graphs, in that mode. */
 int cce_version(void);
 
 /*

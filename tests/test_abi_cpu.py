@@ -47,7 +47,7 @@ def test_status_strings(lib):
         s = cce.status_string(st)
         assert s and s != "unknown status"
     assert cce.status_string(12345) == "unknown status"
-    assert lib.cce_version() == 103
+    assert lib.cce_version() == 104
 
 
 def c2(lib, x=FAKE, w=FAKE, b=None, y=FAKE, N=1, C_in=8, H=16, W=16, C_out=64, k=3):

@@ -2,7 +2,9 @@
 gelu_small): its coefficients, read from the header, must reproduce
 GELU(t) = 0.5 t (1 + erf(t / sqrt 2)) within 2e-8 on [-1, 1] when evaluated
 in double, and within fp32 rounding (2e-7) when evaluated in fp32 the way the
-kernel does (Horner in u = t^2, then u * r + 0.5 t)."""
+kernel does (Horner in u = t^2, then u * r + 0.5 t).  They are the minimax
+fit that channel_convolution_epilogue_amd/gelu_poly_fit.py derives from erf,
+rounded to fp32: refitting reproduces them."""
 import re
 from pathlib import Path
 
@@ -40,3 +42,18 @@ def test_gelu_polynomial_error_bound():
     assert np.abs(y32.astype(np.float64) - exact).max() < 2e-7
     # the t -> 0 limit: slope 1/2 and curvature 1/sqrt(2 pi)
     assert abs(c[-1] - 1.0 / np.sqrt(2.0 * np.pi)) < 1e-6
+
+
+def test_gelu_coefficients_are_the_refit_minimax_polynomial():
+    """Refit P from erf (the committed derivation) and compare with the
+    header: each coefficient is the fit's value rounded to fp32 (within one
+    fp32 ulp, in case the LP solver's last digits differ between platforms),
+    and the fit reaches the minimax error the header's comment states."""
+    from channel_convolution_epilogue_amd import gelu_poly_fit
+    c_fit, err = gelu_poly_fit.fit()
+    assert 3e-9 < err < 5e-9
+    header = coefficients()
+    for got, want in zip(header, c_fit[::-1]):
+        ulp = abs(float(np.spacing(np.float32(want))))
+        assert abs(float(np.float32(got)) - float(np.float32(want))) <= ulp, (got, want)
+        assert abs(got - want) <= 1.5 * ulp

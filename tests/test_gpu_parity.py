@@ -815,3 +815,41 @@ def test_random_shape_sweep_tails(cce):
         y = cce.lrelu_add_clamp_gelu(dev(p["z"]), dev(s), 0.2, -1.0, 1.0)
         torch.cuda.synchronize()
         assert_close(y.cpu().numpy(), O.lrelu_add_clamp_gelu_array(p["z"], s), f"sweep elementwise tail {c}")
+
+
+def test_debug_mode_makes_calls_synchronous():
+    """CCE_DEBUG=1 (read once per process, so in a child process): every
+    launch is followed by a synchronisation of its stream, so an event
+    recorded right after a call has already completed when the call
+    returns, and the results still match the oracle."""
+    import subprocess
+    import sys
+    code = r'''
+import sys, numpy as np, torch
+sys.path.insert(0, ".")
+import channel_convolution_epilogue_amd as cce, oracle as O
+from conv_inputs import CONVT, make_inputs
+cce.load()
+p = make_inputs(CONVT, seed=77, N=24, C_in=64, H=256, W=256, C_out=64, k=3)
+x, w, b = (torch.from_numpy(p[k]).cuda() for k in ("x", "w", "b"))
+y = cce.convT2d_pool_htanh_mean_tanh(x, w, b)
+torch.cuda.synchronize()
+done = []
+for _ in range(3):
+    y = cce.convT2d_pool_htanh_mean_tanh(x, w, b)
+    ev = torch.cuda.Event()
+    ev.record()
+    done.append(ev.query())
+ref = O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], np.arange(0, 24 * 64, 97))
+got = y.cpu().numpy().reshape(-1)[np.arange(0, 24 * 64, 97)]
+ok = np.all(np.abs(got - ref) <= 1e-4 + 1e-4 * np.abs(ref))
+print("DONE", done, "OK", bool(ok), flush=True)
+'''
+    import os
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    env = dict(os.environ, CCE_DEBUG="1")
+    res = subprocess.run([sys.executable, "-c", code], cwd=str(root), env=env, capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode == 0, res.stderr[-3000:]
+    assert "DONE [True, True, True] OK True" in res.stdout, res.stdout + res.stderr[-2000:]
