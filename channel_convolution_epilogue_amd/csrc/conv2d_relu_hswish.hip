@@ -98,11 +98,13 @@ enum Epilogue { kReluHswish = 0, kGeluSeries = 1, kGeluErf = 2 };
 
 // HardSwish(ReLU(v)) = r * clamp((r + 3) / 6, 0, 1) with r = max(v, 0).  For
 // v >= 0 the gate (v + 3) / 6 is at least 0.5, and for v < 0 the result is 0
-// whatever the gate, so the gate can be taken from v itself, clamped to
-// [0.5, 1], and the ReLU applied to the (positive-gated) product:
-// max(v * gate, 0) = max(v, 0) * gate.  Four operations.
+// whatever the (non-negative) gate, so the gate can be taken from v itself,
+// clamped to [0, 1] -- the clamp modifier of the fma, free -- and the ReLU
+// applied to the product: max(v * gate, 0) = max(v, 0) * gate.  Three
+// instructions.  (On gfx950 fp32 MFMAs and plain VALU instructions share one
+// datapath, so every epilogue instruction costs matrix-core time.)
 __device__ __forceinline__ float relu_hswish(float v) {
-  const float gate = __builtin_amdgcn_fmed3f(fmaf(v, 1.0f / 6.0f, 0.5f), 0.5f, 1.0f);
+  const float gate = __builtin_amdgcn_fmed3f(fmaf(v, 1.0f / 6.0f, 0.5f), 0.0f, 1.0f);
   return fmaxf(v * gate, 0.0f);
 }
 
@@ -206,6 +208,11 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   float sadd[NT];  // per-channel term of the GELU epilogue
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) sadd[nt] = EPI == kReluHswish ? 0.0f : a.s[16 * nt + col];
+  // The first K-step's MFMAs start from the bias (as their C operand), so
+  // the accumulators need no initialising copies.
+  v4f bias4[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) bias4[nt] = splat4(bias[nt]);
   if (first >= a.items) return;  // workgroup-uniform
   wstage.place(ws, a.w, tid);
   put();
@@ -233,10 +240,6 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
       for (int jc = 0; jc < CB; ++jc) base[jr * CB + jc] = g * CS + jr * XW + 16 * jc + col + 4 - sh[jr];
     }
     v4f acc[MT][NT];
-#pragma unroll
-    for (int j = 0; j < MT; ++j)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[j][nt] = splat4(bias[nt]);
 
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
@@ -250,7 +253,8 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
 #pragma unroll
       for (int j = 0; j < MT; ++j)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[j][nt] = mfma16x16x4(av[j], bv[nt], acc[j][nt]);
+        for (int nt = 0; nt < NT; ++nt)
+          acc[j][nt] = mfma16x16x4(av[j], bv[nt], s == 0 ? bias4[nt] : acc[j][nt]);
     }
 
     // The window has been read (the MFMAs above consumed every value), so the
