@@ -819,13 +819,16 @@ def test_random_shape_sweep_tails(cce):
 
 def test_debug_mode_makes_calls_synchronous():
     """CCE_DEBUG=1 (read once per process, so in a child process): every
-    launch is followed by a synchronisation of its stream, so an event
-    recorded right after a call has already completed when the call
-    returns, and the results still match the oracle."""
+    launch is followed by a synchronisation of its stream, so each call
+    returns only after its kernel has run -- a call lasts at least the
+    kernel's own GPU time (about 1 ms here, against tens of microseconds for
+    an asynchronous launch) -- and the results still match the oracle."""
+    import os
     import subprocess
     import sys
+    from pathlib import Path
     code = r'''
-import sys, numpy as np, torch
+import sys, time, numpy as np, torch
 sys.path.insert(0, ".")
 import channel_convolution_epilogue_amd as cce, oracle as O
 from conv_inputs import CONVT, make_inputs
@@ -834,22 +837,30 @@ p = make_inputs(CONVT, seed=77, N=24, C_in=64, H=256, W=256, C_out=64, k=3)
 x, w, b = (torch.from_numpy(p[k]).cuda() for k in ("x", "w", "b"))
 y = cce.convT2d_pool_htanh_mean_tanh(x, w, b)
 torch.cuda.synchronize()
-done = []
+e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+ratios = []
 for _ in range(3):
+    e0.record()
+    t0 = time.perf_counter()
     y = cce.convT2d_pool_htanh_mean_tanh(x, w, b)
-    ev = torch.cuda.Event()
-    ev.record()
-    done.append(ev.query())
-ref = O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], np.arange(0, 24 * 64, 97))
-got = y.cpu().numpy().reshape(-1)[np.arange(0, 24 * 64, 97)]
+    call_ms = (time.perf_counter() - t0) * 1e3
+    e1.record()
+    torch.cuda.synchronize()
+    ratios.append(call_ms / e0.elapsed_time(e1))
+idx = np.arange(0, 24 * 64, 97)
+ref = O.convT2d_pool_htanh_mean_tanh_at(p["x"], p["w"], p["b"], idx)
+got = y.cpu().numpy().reshape(-1)[idx]
 ok = np.all(np.abs(got - ref) <= 1e-4 + 1e-4 * np.abs(ref))
-print("DONE", done, "OK", bool(ok), flush=True)
+print("RATIOS", " ".join("%.3f" % r for r in ratios), "OK", bool(ok), flush=True)
 '''
-    import os
-    from pathlib import Path
     root = Path(__file__).resolve().parents[1]
-    env = dict(os.environ, CCE_DEBUG="1")
-    res = subprocess.run([sys.executable, "-c", code], cwd=str(root), env=env, capture_output=True, text=True,
-                         timeout=300)
+    res = subprocess.run([sys.executable, "-c", code], cwd=str(root), env=dict(os.environ, CCE_DEBUG="1"),
+                         capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stderr[-3000:]
-    assert "DONE [True, True, True] OK True" in res.stdout, res.stdout + res.stderr[-2000:]
+    line = [l for l in res.stdout.splitlines() if l.startswith("RATIOS")]
+    assert line, res.stdout + res.stderr[-2000:]
+    parts = line[0].split()
+    ratios = [float(v) for v in parts[1:4]]
+    assert parts[-1] == "True", line[0]
+    # the call spans (almost all of) the event-timed GPU work
+    assert min(ratios) > 0.8, line[0]
