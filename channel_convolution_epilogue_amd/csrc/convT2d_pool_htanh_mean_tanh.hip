@@ -16,9 +16,10 @@
 //  * Implicit GEMM on the fp32 matrix cores: M = conv-output pixels, N =
 //    C_out output channels (16, 32 or 64: one to four 16-column MFMA
 //    blocks), K = C_in channels x 9 taps (576 for the page's layer).  A tile
-//    is 16 x 32 conv pixels (8 x 16 pooling windows) of one image; K is
-//    walked in C_in / 8 chunks of 8 input channels whose input halo tile
-//    (18 x 34) and weight slice (8 x 9 x C_out) are staged in LDS.
+//    is 16 x 32 conv pixels (8 x 16 pooling windows) of one image for 64
+//    output channels (24 x 32 for 32, 32 x 32 for 16); K is walked in
+//    C_in / 8 chunks of 8 input channels whose input halo tile (18 x 34 for
+//    64 channels) and weight slice (8 x 9 x C_out) are staged in LDS.
 //  * The M order puts the four pixels of one 2 x 2 pooling window on four
 //    consecutive M rows, which the matrix core returns in one lane's four
 //    accumulator registers: the max-pool is three in-lane max operations.
@@ -50,27 +51,42 @@ namespace cce {
 namespace {
 
 constexpr int WAVES = 4, THREADS = 64 * WAVES;
-constexpr int TH = 16, TW = 32;             // conv-output pixels per tile
-constexpr int PTH = TH / 2, PTW = TW / 2;   // pooling windows per tile
+constexpr int TW = 32;                      // conv-output columns per tile
+constexpr int PTW = TW / 2;                 // pooling-window columns per tile
 constexpr int CC = 8;                       // input channels per K chunk
-constexpr int XR = TH + 2, XC = TW + 2;     // input halo tile rows / cols
+constexpr int XC = TW + 2;                  // input halo tile columns
 constexpr int XRS = 40;                     // LDS row stride: 8 (mod 64) banks between rows
-constexpr int XCS = XR * XRS;               // 720 = 16 (mod 64): lane groups 16 banks apart
 constexpr int XOFF = 3;                     // LDS column of input column w0 - 1
-constexpr int XS_FLOATS = CC * XCS;
-constexpr int MT = 8;                       // 16-pixel blocks per wave
 
 static_assert(XOFF + XC <= XRS, "halo row fits the LDS row");
 
-// Output-channel geometry: NT 16-column MFMA blocks; the weight slice of one
-// K chunk holds (CC / 4) x 9 x 64 lanes x NT floats.
+// Geometry per output-channel count: NT 16-column MFMA blocks; every wave
+// computes MT 16-pixel blocks, RP = MT / 4 row pairs of the tile's 32
+// columns, so a tile has TH = 8 RP rows.  With 64 channels (NT = 4) 8 blocks
+// per wave fill 128 accumulator registers (16 x 32 tiles); with fewer
+// channels a wave takes more blocks -- 12 for 32 channels (24 x 32 tiles), 16
+// for 16 (32 x 32) -- so that each staged chunk and each barrier carry more
+// MFMAs, within the register budget of two waves per SIMD.  The weight slice
+// of one K chunk holds (CC / 4) x 9 x 64 lanes x NT floats.
 template <int CO_>
 struct OutCh {
   static constexpr int CO = CO_, NT = CO / 16;
+  static constexpr int MT = NT == 4 ? 8 : NT == 2 ? 12 : 16, RP = MT / 4;
+  static constexpr int TH = 2 * RP * WAVES, PTH = TH / 2;  // conv-output / pooled rows per tile
+  static constexpr int XR = TH + 2;                      // input halo tile rows
+  static constexpr int XCS = XR * XRS;  // 16 (mod 64): the lane groups' channels 16 banks apart
+  static constexpr int XS_FLOATS = CC * XCS;
   static constexpr int WS_FLOATS = (CC / 4) * 9 * 64 * NT;
   static constexpr int W4_PER_CHUNK = WS_FLOATS / 4;
   static constexpr int W4_PT = (W4_PER_CHUNK + THREADS - 1) / THREADS;
+  // Per-chunk input staging in 16-byte units (interior) and single floats (halo columns).
+  static constexpr int XQ = TW / 4;                                  // 8 float4 per row
+  static constexpr int X4_PER_CHUNK = CC * XR * XQ;
+  static constexpr int X4_PT = (X4_PER_CHUNK + THREADS - 1) / THREADS;
+  static constexpr int XH_PER_CHUNK = CC * XR * 2;
+  static constexpr int XH_PT = (XH_PER_CHUNK + THREADS - 1) / THREADS;
   static_assert(CO == 16 || CO == 32 || CO == 64, "C_out is 16, 32 or 64");
+  static_assert(XCS % 64 == 16, "lane groups' channel planes 16 banks apart");
 };
 
 struct ConvTArgs {
@@ -92,18 +108,13 @@ struct ConvTArgs {
 // each (channel, row) are four-aligned in the image (w0 % 32 == 0, W % 4 == 0)
 // and land on four-aligned LDS columns (XOFF + 1 = 4); the two halo columns
 // are single floats.
-constexpr int XQ = TW / 4;                                         // 8 float4 per row
-constexpr int X4_PER_CHUNK = CC * XR * XQ;                         // 1152
-constexpr int X4_PT = (X4_PER_CHUNK + THREADS - 1) / THREADS;      // 5
-constexpr int XH_PER_CHUNK = CC * XR * 2;                          // 288 halo floats
-constexpr int XH_PT = (XH_PER_CHUNK + THREADS - 1) / THREADS;      // 2
 static_assert(XOFF + 1 == 4, "interior columns start 16-byte aligned in LDS");
 
 template <class OC>
 struct ChunkRegs {
   v4f w4[OC::W4_PT];
-  v4f x4[X4_PT];
-  float xh[XH_PT];
+  v4f x4[OC::X4_PT];
+  float xh[OC::XH_PT];
 };
 
 // Global -> registers for channel chunk c (issued a whole chunk ahead of use).
@@ -120,12 +131,12 @@ __device__ __forceinline__ void load_chunk(const ConvTArgs &a, int n, int c, int
   }
   const float *xc = a.x + ((size_t)n * a.C_in + CC * c) * a.H * a.W;
 #pragma unroll
-  for (int j = 0; j < X4_PT; ++j) {
+  for (int j = 0; j < OC::X4_PT; ++j) {
     const int i = tid + j * THREADS;
     v4f v = splat4(0.0f);
-    if (i < X4_PER_CHUNK) {
-      const int row = i / XQ, q = i - row * XQ;  // row = cl * XR + rr
-      const int cl = row / XR, rr = row - cl * XR;
+    if (i < OC::X4_PER_CHUNK) {
+      const int row = i / OC::XQ, q = i - row * OC::XQ;  // row = cl * OC::XR + rr
+      const int cl = row / OC::XR, rr = row - cl * OC::XR;
       const int h = h0 - 1 + rr, wc = w0 + 4 * q;
       if (h >= 0 && h < a.H) {
         const float *src = xc + ((size_t)cl * a.H + h) * a.W + wc;
@@ -142,12 +153,12 @@ __device__ __forceinline__ void load_chunk(const ConvTArgs &a, int n, int c, int
     r.x4[j] = v;
   }
 #pragma unroll
-  for (int j = 0; j < XH_PT; ++j) {
+  for (int j = 0; j < OC::XH_PT; ++j) {
     const int i = tid + j * THREADS;
     float v = 0.0f;
-    if (i < XH_PER_CHUNK) {
+    if (i < OC::XH_PER_CHUNK) {
       const int row = i >> 1, side = i & 1;
-      const int cl = row / XR, rr = row - cl * XR;
+      const int cl = row / OC::XR, rr = row - cl * OC::XR;
       const int h = h0 - 1 + rr, wc = side ? w0 + TW : w0 - 1;
       if (h >= 0 && h < a.H && wc >= 0 && wc < a.W) v = xc[((size_t)cl * a.H + h) * a.W + wc];
     }
@@ -164,21 +175,21 @@ __device__ __forceinline__ void store_chunk(float *xs, float *ws, int tid, const
     if (i < OC::W4_PER_CHUNK) reinterpret_cast<v4f *>(ws)[i] = r.w4[j];
   }
 #pragma unroll
-  for (int j = 0; j < X4_PT; ++j) {
+  for (int j = 0; j < OC::X4_PT; ++j) {
     const int i = tid + j * THREADS;
-    if (i < X4_PER_CHUNK) {
-      const int row = i / XQ, q = i - row * XQ;
-      const int cl = row / XR, rr = row - cl * XR;
-      *reinterpret_cast<v4f *>(&xs[cl * XCS + rr * XRS + XOFF + 1 + 4 * q]) = r.x4[j];
+    if (i < OC::X4_PER_CHUNK) {
+      const int row = i / OC::XQ, q = i - row * OC::XQ;
+      const int cl = row / OC::XR, rr = row - cl * OC::XR;
+      *reinterpret_cast<v4f *>(&xs[cl * OC::XCS + rr * XRS + XOFF + 1 + 4 * q]) = r.x4[j];
     }
   }
 #pragma unroll
-  for (int j = 0; j < XH_PT; ++j) {
+  for (int j = 0; j < OC::XH_PT; ++j) {
     const int i = tid + j * THREADS;
-    if (i < XH_PER_CHUNK) {
+    if (i < OC::XH_PER_CHUNK) {
       const int row = i >> 1, side = i & 1;
-      const int cl = row / XR, rr = row - cl * XR;
-      xs[cl * XCS + rr * XRS + (side ? XOFF + 1 + TW : XOFF)] = r.xh[j];
+      const int cl = row / OC::XR, rr = row - cl * OC::XR;
+      xs[cl * OC::XCS + rr * XRS + (side ? XOFF + 1 + TW : XOFF)] = r.xh[j];
     }
   }
 }
@@ -215,8 +226,8 @@ __global__ __launch_bounds__(THREADS) void convT_prepare_weight_kernel(const flo
 template <class OC, bool VEC, int NCH>
 __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kernel(ConvTArgs a) {
   const int nchunk = NCH > 0 ? NCH : a.nchunk;
-  constexpr int CO = OC::CO, NT = OC::NT;
-  __shared__ __attribute__((aligned(16))) float xs[XS_FLOATS];
+  constexpr int CO = OC::CO, NT = OC::NT, MT = OC::MT, RP = OC::RP, XCS = OC::XCS;
+  __shared__ __attribute__((aligned(16))) float xs[OC::XS_FLOATS];
   __shared__ __attribute__((aligned(16))) float ws[OC::WS_FLOATS];
   __shared__ float red[THREADS];  // [WAVES][CO], then [THREADS / CO][CO]
   __shared__ int last_flag;
@@ -232,12 +243,14 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
   const int n = tile / a.tiles_per_image;
   const int ti = tile - n * a.tiles_per_image;
   const int ty = ti / a.tiles_x, tx = ti - ty * a.tiles_x;
-  const int h0 = ty * TH, w0 = tx * TW;
+  const int h0 = ty * OC::TH, w0 = tx * TW;
 
   // A-operand lane: M row m = col -> pooling window col/4 of the block, pixel
   // (dh, dw) = ((col & 3) >> 1, col & 1) inside it; lane group g = channel.
+  // Wave w covers the tile's rows 2 RP w .. 2 RP w + 2 RP - 1; block mt its
+  // row pair mt / 4 and columns 8 (mt % 4) .. + 7.
   const int wi = col >> 2, dh = (col & 3) >> 1, dw = col & 1;
-  const int abase = g * XCS + (4 * wave + dh) * XRS + XOFF + 2 * wi + dw;
+  const int abase = g * XCS + (2 * RP * wave + dh) * XRS + XOFF + 2 * wi + dw;
 
   v4f acc[MT][NT];
 #pragma unroll
@@ -279,17 +292,17 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
   }
 
   // Epilogue: lane holds, per block and channel block, the 4 pixels of pooling
-  // window (ph, pw) = (ph0 + 2 wave + mt/4, pw0 + 4 (mt%4) + g), channel 16 nt + col.
+  // window (ph, pw) = (ph0 + RP wave + mt/4, pw0 + 4 (mt%4) + g), channel 16 nt + col.
   float bias[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
   float sum[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) sum[nt] = 0.0f;
-  const int ph0 = ty * PTH, pw0 = tx * PTW;
+  const int ph0 = ty * OC::PTH, pw0 = tx * PTW;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int ph = ph0 + 2 * wave + (mt >> 2), pw = pw0 + 4 * (mt & 3) + g;
+    const int ph = ph0 + RP * wave + (mt >> 2), pw = pw0 + 4 * (mt & 3) + g;
     const bool valid = ph < a.PH && pw < a.PW;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -346,10 +359,13 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
 
 constexpr size_t kTicketAlign = 256;
 
-void convT_tiles(int H, int W, int *tiles_x, int *tiles_per_image) {
+// Tiles of a layer: 16 pooling-window columns by OutCh<C_out>::PTH rows (8
+// for 64 output channels, 12 for 32, 16 for 16).
+void convT_tiles(int H, int W, int C_out, int *tiles_x, int *tiles_per_image) {
   const int PH = H / 2, PW = W / 2;
+  const int pth = C_out == 64 ? OutCh<64>::PTH : C_out == 32 ? OutCh<32>::PTH : OutCh<16>::PTH;
   *tiles_x = (PW + PTW - 1) / PTW;
-  *tiles_per_image = ((PH + PTH - 1) / PTH) * *tiles_x;
+  *tiles_per_image = ((PH + pth - 1) / pth) * *tiles_x;
 }
 
 
@@ -387,7 +403,7 @@ bool convT_layer_supported(int C_in, int C_out) {
 // Workspace: [per-image counters, padded to 256 B][prepared weight][partials].
 size_t convT_workspace_bytes(int N, int C_in, int H, int W, int C_out) {
   int tx, tpi;
-  convT_tiles(H, W, &tx, &tpi);
+  convT_tiles(H, W, C_out, &tx, &tpi);
   return ticket_bytes(N) + wprep_bytes(C_in, C_out) + (size_t)N * tpi * C_out * sizeof(float);
 }
 
@@ -406,7 +422,7 @@ int launch_convT2d_pool_htanh_mean_tanh(const float *x, const float *w, const fl
   a.W = W;
   a.PH = H / 2;  // conv output is H x W at stride 1, padding 1; floor pooling
   a.PW = W / 2;
-  convT_tiles(H, W, &a.tiles_x, &a.tiles_per_image);
+  convT_tiles(H, W, C_out, &a.tiles_x, &a.tiles_per_image);
   a.lo = lo;
   a.hi = hi;
   a.inv_count = (float)(1.0 / ((double)a.PH * (double)a.PW));
