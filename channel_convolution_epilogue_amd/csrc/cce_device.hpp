@@ -23,6 +23,32 @@ __device__ __forceinline__ v4f mfma16x16x4(float a, float b, v4f c) {
 
 __device__ __forceinline__ v4f splat4(float v) { return v4f{v, v, v, v}; }
 
+// Raw buffer accesses (MUBUF, offset addressing): a 128-bit descriptor holds
+// the base address and the buffer's size in bytes, and each lane supplies a
+// 32-bit byte offset.  A load whose offset lies at or past the size returns
+// zeros without touching memory, so masked window loads need no branch:
+// such a lane is given kBufferOOB as its offset (buffers here are smaller
+// than 2^31 bytes).  Dword 3 = 0x00020000 selects 32-bit data elements.
+constexpr uint32_t kBufferOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ void buffer_store1(__amdgpu_buffer_rsrc_t r, float v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)voff, 0, 0);
+}
+
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, v4f v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)voff, (int)soff, 0);
+}
+
 // Stages a [CO][CI][TAPS] convolution weight (the torch layout) into LDS in
 // MFMA B-operand order: K-step s covers input channels 4 (s / TAPS) .. + 3 at
 // tap s % TAPS, and

@@ -27,6 +27,13 @@
 //    (row offset mod 4) columns so that every lane's four pixels start on a
 //    16-byte boundary even when the row length is not a multiple of four;
 //    pixels that fall outside the row are masked.
+//  * Window loads and result stores are raw buffer accesses over one image,
+//    with 32-bit lane offsets: a position outside the image gets an offset
+//    past the buffer's end, which loads zeros (or drops the store), so no
+//    lane branches and the per-strip address arithmetic is a few adds.  On
+//    gfx950 fp32 MFMAs and plain VALU instructions share one datapath, so
+//    this arithmetic is matrix-core time: the checked global loads and
+//    stores they replace cost 5-7 % of the kernel.
 //  * The K order puts the four lane groups on four input channels and one
 //    (channel half, kh, kw) per step, so the step's LDS offset is the same for
 //    all lanes.  The 72 x 64 weight sits in LDS in B-operand order: one
@@ -160,7 +167,32 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   v4f pre[VLOAD ? PER_LANE : 1];
   float pres[VLOAD ? 1 : PER_LANE];
   // One image is less than 2^31 floats, so in-image offsets are 32-bit.
+  // VLOAD: buffer loads over one image (less than 2^31 bytes), with
+  // positions outside it given the out-of-range offset, which loads zeros.
+  // Per lane and quad f: the staged row, the column offset from c0 and the
+  // byte offset within the image relative to (row r0, column c0).
+  int lrow[VLOAD ? PER_LANE : 1], ldc[VLOAD ? PER_LANE : 1], lofs[VLOAD ? PER_LANE : 1];
+#pragma unroll
+  for (int f = 0; f < (VLOAD ? PER_LANE : 1); ++f) {
+    // Lanes past the window's last quad repeat quad e % UNITS (same data to
+    // the same LDS address), so every lane loads and stores unconditionally.
+    const int e = (lane + 64 * f) % UNITS;
+    const int cq = e % XQ, rc = e / XQ, row = rc % ROWS, ch = rc / ROWS;
+    lrow[f] = row;
+    ldc[f] = 4 * cq - 4;
+    lofs[f] = ((ch * a.H + row) * a.W + 4 * cq - 4) * 4;
+  }
   auto load = [&](const Strip &s) {
+    if constexpr (VLOAD) {
+      const auto rx = buffer_rsrc(a.x + (size_t)s.n * CI * a.H * a.W, (uint32_t)(CI * a.H * a.W) * 4u);
+      const int uni = (s.r0 * a.W + s.c0) * 4, rows_left = a.H - s.r0;
+#pragma unroll
+      for (int f = 0; f < PER_LANE; ++f) {
+        const bool ok = lrow[f] < rows_left && (unsigned)(s.c0 + ldc[f]) < (unsigned)a.W;
+        pre[f] = buffer_load4(rx, ok ? (uint32_t)(lofs[f] + uni) : kBufferOOB, 0u);
+      }
+      return;
+    }
     const float *xs = a.x + (size_t)s.n * CI * a.H * a.W + s.r0 * a.W + s.c0;
 #pragma unroll
     for (int f = 0; f < PER_LANE; ++f) {
@@ -181,7 +213,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   auto put = [&]() {
 #pragma unroll
     for (int f = 0; f < PER_LANE; ++f) {
-      const int e = lane + 64 * f;
+      const int e = VLOAD ? (lane + 64 * f) % UNITS : lane + 64 * f;
       if (e < UNITS) {
         const int per_row = VLOAD ? XQ : XW;
         const int cq = e % per_row, rc = e / per_row, row = rc % ROWS, ch = rc / ROWS;
@@ -213,6 +245,9 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   v4f bias4[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bias4[nt] = splat4(bias[nt]);
+  // Byte offset of this lane's result quad within channel block 0's planes,
+  // relative to a strip's first output pixel.
+  const int sofs = VSTORE ? (col * a.P + 4 * g) * 4 : 0;
   if (first >= a.items) return;  // workgroup-uniform
   wstage.place(ws, a.w, tid);
   put();
@@ -227,6 +262,9 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
     // so the compiler's wait counts never hold a later load behind a store.
     const Strip nxt = more ? decode(next) : cur;
     load(nxt);  // in flight during this strip's MFMAs
+    // Keep the loads here: the scheduler would otherwise sink them to their
+    // use after the MFMAs.
+    __builtin_amdgcn_sched_barrier(0);
 
     // Block (jr, jc) covers output row r0 + jr, columns
     // [c0 + 16 jc - sh, c0 + 16 jc - sh + 16) with sh = (row offset) mod 4, so
@@ -279,22 +317,46 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
         acc[j][nt].w = epilogue(acc[j][nt].w, nt);
       }
 
+    if constexpr (VSTORE) {
+      // Buffer stores over one image's output (less than 2^31 bytes): the
+      // lane's byte offset in channel block 0 as the vector offset, block
+      // nt's plane offset as the scalar one.  A lane quad that crosses a row
+      // end or start stores its in-row pixels one by one; the others get the
+      // out-of-range offset, which drops their stores.
+      const auto ry = buffer_rsrc(a.y + (size_t)cur.n * CO * a.P, (uint32_t)(CO * a.P) * 4u);
 #pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      const int jr = j / CB, jc = j % CB, r = cur.r0 + jr;
-      if (r >= a.Ho || !valid) break;
-      const int cb = cur.c0 + 16 * jc - sh[jr] + 4 * g;  // this lane's first output column
-      float *dst = a.y + (size_t)cur.n * CO * a.P + (size_t)r * a.Wo + cb;
+      for (int j = 0; j < MT; ++j) {
+        const int jr = j / CB, jc = j % CB, r = cur.r0 + jr;
+        if (r >= a.Ho || !valid) break;
+        const int c = cur.c0 + 16 * jc - sh[jr];  // the block's first output column
+        const int cb = c + 4 * g;                 // this lane's
+        const uint32_t voff = (uint32_t)(sofs + (r * a.Wo + c) * 4);
+        if (cb >= 0 && cb + 3 < a.Wo) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const v4f v = acc[j][nt];
-        float *d = dst + (size_t)(16 * nt + col) * a.P;
-        if (VSTORE && cb >= 0 && cb + 3 < a.Wo) {
-          store4(d, v);
+          for (int nt = 0; nt < NT; ++nt) buffer_store4(ry, acc[j][nt], voff, (uint32_t)(16 * nt * a.P) * 4u);
         } else {
 #pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool in_row = cb + e >= 0 && cb + e < a.Wo;
+              buffer_store1(ry, acc[j][nt][e], in_row ? voff + (uint32_t)(16 * nt * a.P + e) * 4u : kBufferOOB);
+            }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        const int jr = j / CB, jc = j % CB, r = cur.r0 + jr;
+        if (r >= a.Ho || !valid) break;
+        const int cb = cur.c0 + 16 * jc + 4 * g;  // this lane's first output column
+        float *dst = a.y + (size_t)cur.n * CO * a.P + (size_t)r * a.Wo + cb;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float *d = dst + (size_t)(16 * nt + col) * a.P;
+#pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (cb + e >= 0 && cb + e < a.Wo) d[e] = v[e];
+            if (cb + e < a.Wo) d[e] = acc[j][nt][e];
         }
       }
     }
@@ -353,8 +415,9 @@ int launch_layer(const float *x, const float *w, const float *b, float *y, int N
   a.Wo = W - (GEO::KS - 1);
   a.P = a.Ho * a.Wo;
 
-  const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
-  const bool vs = (a.P % 4 == 0) && ((uintptr_t)y % 16 == 0);
+  // The 16-byte paths address one image through 32-bit buffer offsets.
+  const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0) && (long long)GEO::CI * H * W * 4 < (1LL << 31);
+  const bool vs = (a.P % 4 == 0) && ((uintptr_t)y % 16 == 0) && (long long)GEO::CO * a.P * 4 < (1LL << 31);
   // Largest left shift any row's strips take (0 when stores are scalar).
   int sh_max = 0;
   if (vs)

@@ -531,8 +531,10 @@ def gather(y, idx):
 
 def test_conv2d_output_near_index_limit(cce):
     """One 5790 x 5788 image: N * C_out * Ho * Wo = 2,143,319,552, within 0.2 %
-    of the 2^31 output limit, on the tuned 16-byte instance (W and the plane
-    are multiples of 4); checked at sampled outputs including the last ones."""
+    of the 2^31 output limit (W and the plane are multiples of 4: 16-byte
+    window loads; the 8.6 GB output plane set is past the 2^31-byte range of
+    the buffer stores, so results leave through the scalar store path);
+    checked at sampled outputs including the last ones."""
     p = make_inputs(CONV2D, seed=81, N=1, C_in=8, H=5790, W=5788, C_out=64, k=3)
     y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
     torch.cuda.synchronize()
@@ -544,6 +546,26 @@ def test_conv2d_output_near_index_limit(cce):
     del y
     torch.cuda.empty_cache()
     assert_close(got, O.conv2d_relu_hswish_at(p["x"], p["w"], p["b"], idx), "conv2d near 2^31 outputs")
+
+
+@pytest.mark.parametrize("C_in,C_out,k,H,W", [
+    (8, 64, 3, 2896, 2900),   # output 2,147,023,872 bytes: 16-byte loads and stores
+    (16, 16, 1, 5800, 5800),  # input 2,152,960,000 bytes: past the buffer loads' range
+])
+def test_conv2d_buffer_range_limits(cce, C_in, C_out, k, H, W):
+    """The 16-byte paths address one image through 32-bit buffer offsets and
+    take images below 2^31 bytes; at and just past that size (sampled outputs,
+    the last ones included) the results still match the oracle."""
+    p = make_inputs(CONV2D, seed=83, N=1, C_in=C_in, H=H, W=W, C_out=C_out, k=k)
+    y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
+    torch.cuda.synchronize()
+    total = y.numel()
+    idx = np.unique(np.concatenate([sample_indices(total, 3000, 83), np.arange(total - 300, total),
+                                    np.arange(200)]))
+    got = gather(y, idx)
+    del y
+    torch.cuda.empty_cache()
+    assert_close(got, O.conv2d_relu_hswish_at(p["x"], p["w"], p["b"], idx), "conv2d buffer range limits")
 
 
 def test_conv3d_output_near_index_limit(cce):
