@@ -45,8 +45,12 @@ __device__ __forceinline__ void buffer_store1(__amdgpu_buffer_rsrc_t r, float v,
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)voff, 0, 0);
 }
 
-__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, v4f v, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)voff, (int)soff, 0);
+// The scalar offset of a store stays the constant 0: with an SGPR there the
+// compiler inserts no wait states between a 16-byte store and a following
+// VALU write of its data registers, and on gfx950 such a write was seen to
+// reach memory in place of the stored data for some lanes.
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, v4f v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)voff, 0, 0);
 }
 
 // Stages a [CO][CI][TAPS] convolution weight (the torch layout) into LDS in

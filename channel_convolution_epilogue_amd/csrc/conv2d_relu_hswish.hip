@@ -318,9 +318,9 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
       }
 
     if constexpr (VSTORE) {
-      // Buffer stores over one image's output (less than 2^31 bytes): the
-      // lane's byte offset in channel block 0 as the vector offset, block
-      // nt's plane offset as the scalar one.  A lane quad that crosses a row
+      // Buffer stores over one image's output (less than 2^31 bytes), at the
+      // lane's byte offset in channel block 0 plus block nt's plane offset.
+      // A lane quad that crosses a row
       // end or start stores its in-row pixels one by one; the others get the
       // out-of-range offset, which drops their stores.
       const auto ry = buffer_rsrc(a.y + (size_t)cur.n * CO * a.P, (uint32_t)(CO * a.P) * 4u);
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
         const uint32_t voff = (uint32_t)(sofs + (r * a.Wo + c) * 4);
         if (cb >= 0 && cb + 3 < a.Wo) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) buffer_store4(ry, acc[j][nt], voff, (uint32_t)(16 * nt * a.P) * 4u);
+          for (int nt = 0; nt < NT; ++nt) buffer_store4(ry, acc[j][nt], voff + (uint32_t)(16 * nt * a.P) * 4u);
         } else {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)

@@ -186,6 +186,21 @@ def test_conv3d_other_epilogue_parameters(cce):
         assert_close(y.cpu().numpy(), ref, f"conv3d slope={slope} clamp=[{lo},{hi}]")
 
 
+@pytest.mark.parametrize("N,D,H,W,lo,hi", [
+    (2, 3, 11, 64, -2.0, 1.5),   # one output plane per block: only the last-tile reload
+    (1, 7, 66, 64, -1.0, 1.0),   # 8 row blocks, the last of 8 rows; odd depth
+    (3, 5, 13, 64, -0.5, 0.75),  # two row blocks, the second of 3 rows
+])
+def test_conv3d_page_layer_instance_edges(cce, N, D, H, W, lo, hi):
+    """The page's layer on 64-wide rows (buffer-staged planes, buffer stores)
+    at block and depth edges, with the polynomial GELU and with erff."""
+    p = make_inputs(CONV3D, seed=260 + D + H, N=N, C_in=8, D=D, H=H, W=W, C_out=64, k=3)
+    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, lo, hi)
+    torch.cuda.synchronize()
+    ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"], 0.2, lo, hi)
+    assert_close(y.cpu().numpy(), ref, f"conv3d N={N} {D}x{H}x{W} clamp [{lo}, {hi}]")
+
+
 def test_conv3d_workload_n128_full(cce):
     """Every one of the 440,860,672 outputs against the oracle, eight images
     at a time (the oracle's double output for the whole batch would be 3.5 GB)."""
