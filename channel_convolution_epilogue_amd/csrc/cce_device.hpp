@@ -89,11 +89,14 @@ struct WeightStageB {
     }
   }
 
-  __device__ __forceinline__ void place(float *ws, const float *__restrict__ w, int tid) const {
+  // scale: a power of two the weights are multiplied by (exactly) on the
+  // way into LDS.
+  __device__ __forceinline__ void place(float *ws, const float *__restrict__ w, int tid,
+                                        float scale = 1.0f) const {
     auto put = [&](int o, int r, float x) {
       const int ci = r / TAPS, tap = r - ci * TAPS;
       const int s = (ci >> 2) * TAPS + tap, lane = ((ci & 3) << 4) | (o & 15);
-      ws[(s * 64 + lane) * NT + (o >> 4)] = x;
+      ws[(s * 64 + lane) * NT + (o >> 4)] = x * scale;
     };
     if (vec) {
 #pragma unroll
@@ -117,10 +120,11 @@ struct WeightStageB {
 };
 
 template <int CI, int CO, int TAPS, int THREADS>
-__device__ __forceinline__ void stage_weights_b(float *ws, const float *__restrict__ w, int tid) {
+__device__ __forceinline__ void stage_weights_b(float *ws, const float *__restrict__ w, int tid,
+                                                float scale = 1.0f) {
   WeightStageB<CI, CO, TAPS, THREADS> st;
   st.load(w, tid);
-  st.place(ws, w, tid);
+  st.place(ws, w, tid, scale);
 }
 
 // A lane's MFMA B operands of one K-step for NT 16-column channel blocks,
@@ -153,14 +157,32 @@ __device__ __forceinline__ float clampf(float v, float lo, float hi) {
 // GELU -- below the fp32 rounding of the evaluation itself (about 1e-7).
 // Four FMAs where the Maclaurin series of erf needs seven for the same
 // accuracy.
+constexpr float kGeluP4 = 9.09758819e-05f, kGeluP3 = -0.00116171606f, kGeluP2 = 0.00996111613f,
+                kGeluP1 = -0.0664877221f, kGeluP0 = 0.398942083f;
+
 __device__ __forceinline__ float gelu_small(float t) {
   const float u = t * t;
-  float r = 9.09758819e-05f;
-  r = fmaf(r, u, -0.00116171606f);
-  r = fmaf(r, u, 0.00996111613f);
-  r = fmaf(r, u, -0.0664877221f);
-  r = fmaf(r, u, 0.398942083f);
+  float r = kGeluP4;
+  r = fmaf(r, u, kGeluP3);
+  r = fmaf(r, u, kGeluP2);
+  r = fmaf(r, u, kGeluP1);
+  r = fmaf(r, u, kGeluP0);
   return fmaf(u, r, 0.5f * t);
+}
+
+// GELU(2 h) for |h| <= 1/2, from h itself: with u' = h^2 = u / 4 and
+// Q(x) = 4 P(4 x), whose coefficients 4^(k+1) p_k are P's scaled by powers
+// of two (exactly), GELU(t) = u' Q(u') + h.  Every intermediate is the one
+// of gelu_small(2 h) scaled by a power of two, so the result is the same to
+// the bit, and the 0.5 t product is gone.
+__device__ __forceinline__ float gelu_small_half(float h) {
+  const float u = h * h;
+  float r = 1024.0f * kGeluP4;
+  r = fmaf(r, u, 256.0f * kGeluP3);
+  r = fmaf(r, u, 64.0f * kGeluP2);
+  r = fmaf(r, u, 16.0f * kGeluP1);
+  r = fmaf(r, u, 4.0f * kGeluP0);
+  return fmaf(u, r, h);
 }
 
 // LeakyReLU -> + s -> clamp -> GELU.  SERIES: the clamp bounds lie in [-1, 1],
@@ -175,6 +197,22 @@ __device__ __forceinline__ float lrelu_add_clamp_gelu_value(float v, float s, fl
   const float c = __builtin_amdgcn_fmed3f(t + s, lo, hi);
   if (SERIES) return gelu_small(c);
   return 0.5f * c * (1.0f + erff(c * 0.70710678118654752f));
+}
+
+// The same chain on halved values: h = v / 2, s_half = s / 2, lo_half and
+// hi_half the halved bounds (a kernel whose weights and bias are staged at
+// half scale produces h directly).  Halving commutes with every rounding in
+// the chain, and GELU(c) = 0.5 c (1 + erf(c / sqrt 2)) becomes
+// c' (1 + erf(c' sqrt 2)) with c' = c / 2 (fp32 sqrt 2 is exactly twice fp32
+// 1 / sqrt 2), so the result equals lrelu_add_clamp_gelu_value(v, ...) bit
+// for bit, with one multiplication fewer.
+template <bool SERIES>
+__device__ __forceinline__ float lrelu_add_clamp_gelu_half(float h, float s_half, float slope, float lo_half,
+                                                           float hi_half) {
+  const float t = __builtin_amdgcn_fmed3f(h, slope * h, slope <= 1.0f ? INFINITY : -INFINITY);
+  const float c = __builtin_amdgcn_fmed3f(t + s_half, lo_half, hi_half);
+  if (SERIES) return gelu_small_half(c);
+  return c * (1.0f + erff(c * 1.41421356237309515f));
 }
 
 // Division of a non-negative 31-bit integer by a divisor fixed per launch,

@@ -171,14 +171,17 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
   const int g = lane >> 4, col = lane & 15;
 
   // ws[s][lane][nt] = w[16 nt + lane % 16][4 (s / TAPS) + lane / 16][tap s % TAPS].
-  stage_weights_b<CI, CO, TAPS, THREADS>(ws, a.w, tid);
-  // Bias and the added per-channel term, read from LDS when needed (fewer
-  // live registers): ep[c] = b[c], ep[64 + c] = s[c].
+  // At half scale (exact): the accumulators then hold v / 2, and the
+  // epilogue on halved values skips one multiplication per output.
+  stage_weights_b<CI, CO, TAPS, THREADS>(ws, a.w, tid, 0.5f);
+  // Bias and the added per-channel term, halved, read from LDS when needed
+  // (fewer live registers): ep[c] = b[c] / 2, ep[64 + c] = s[c] / 2.
   float *ep = xs + CI * chstride;
   if (tid < CO) {
-    ep[tid] = a.b ? a.b[tid] : 0.0f;
-    ep[CO + tid] = a.s[tid];
+    ep[tid] = a.b ? 0.5f * a.b[tid] : 0.0f;
+    ep[CO + tid] = 0.5f * a.s[tid];
   }
+  const float lo_half = 0.5f * a.lo, hi_half = 0.5f * a.hi;
   // Output voxels per (n, channel); one image's output is below 2^31 floats,
   // so offsets within it are 32-bit.
   const int vol = a.Do * a.Ho * a.Wo;
@@ -324,10 +327,10 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
               for (int nt = 0; nt < NT; ++nt) {
                 const float sadd = ep[CO + 16 * nt + col];
                 v4f r = acc[j][nt];
-                r.x = lrelu_add_clamp_gelu_value<SERIES>(r.x, sadd, a.slope, a.lo, a.hi);
-                r.y = lrelu_add_clamp_gelu_value<SERIES>(r.y, sadd, a.slope, a.lo, a.hi);
-                r.z = lrelu_add_clamp_gelu_value<SERIES>(r.z, sadd, a.slope, a.lo, a.hi);
-                r.w = lrelu_add_clamp_gelu_value<SERIES>(r.w, sadd, a.slope, a.lo, a.hi);
+                r.x = lrelu_add_clamp_gelu_half<SERIES>(r.x, sadd, a.slope, lo_half, hi_half);
+                r.y = lrelu_add_clamp_gelu_half<SERIES>(r.y, sadd, a.slope, lo_half, hi_half);
+                r.z = lrelu_add_clamp_gelu_half<SERIES>(r.z, sadd, a.slope, lo_half, hi_half);
+                r.w = lrelu_add_clamp_gelu_half<SERIES>(r.w, sadd, a.slope, lo_half, hi_half);
                 buffer_store4(ry, r, voff + (uint32_t)(16 * nt * vol) * 4u);
               }
             }
@@ -352,10 +355,10 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
           for (int nt = 0; nt < NT; ++nt) {
             const float sadd = ep[CO + 16 * nt + col];
             v4f r = acc[j][nt];
-            r.x = lrelu_add_clamp_gelu_value<SERIES>(r.x, sadd, a.slope, a.lo, a.hi);
-            r.y = lrelu_add_clamp_gelu_value<SERIES>(r.y, sadd, a.slope, a.lo, a.hi);
-            r.z = lrelu_add_clamp_gelu_value<SERIES>(r.z, sadd, a.slope, a.lo, a.hi);
-            r.w = lrelu_add_clamp_gelu_value<SERIES>(r.w, sadd, a.slope, a.lo, a.hi);
+            r.x = lrelu_add_clamp_gelu_half<SERIES>(r.x, sadd, a.slope, lo_half, hi_half);
+            r.y = lrelu_add_clamp_gelu_half<SERIES>(r.y, sadd, a.slope, lo_half, hi_half);
+            r.z = lrelu_add_clamp_gelu_half<SERIES>(r.z, sadd, a.slope, lo_half, hi_half);
+            r.w = lrelu_add_clamp_gelu_half<SERIES>(r.w, sadd, a.slope, lo_half, hi_half);
             float *dst = ytile + ((16 * nt + col) * vol + off0);
             if (VSTORE && run >= 4) {
               store4(dst, r);
