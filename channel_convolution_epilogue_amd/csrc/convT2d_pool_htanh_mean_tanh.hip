@@ -27,8 +27,9 @@
 //    max(z + b) exactly), then Hardtanh, then the window sums are reduced
 //    lane -> wave (cross-lane shuffles) -> workgroup (LDS).
 //  * Each workgroup stores its 64 partial sums and bumps a per-image counter
-//    (agent-scope acquire/release); the workgroup that completes an image
-//    adds that image's partials in a fixed order and applies mean and tanh.
+//    (an agent-scope release); the workgroup that completes an image
+//    acquires, adds that image's partials in a fixed order and applies mean
+//    and tanh.
 //    The result is deterministic.  A small kernel launched just before the
 //    main one zeroes the counters and writes the prepared weight.
 //  * XCD-aware tile order: each of the 8 XCDs takes one contiguous range of
@@ -328,11 +329,20 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  // The counter update releases this workgroup's partials (its stores, all
+  // from wave 0, come before it in program order, the other waves' work
+  // through the barrier above); only the workgroup that completes the image
+  // acquires, below.  (An acquire on every update, or a separate fence before
+  // it, costs 2 % of the page's layer at N = 128: each one writes back or
+  // invalidates this XCD's L2.)
   if (tid == 0) {
-    __threadfence();
-    const unsigned done = __hip_atomic_fetch_add(&a.tickets[n], 1u, __ATOMIC_ACQ_REL,
+    const unsigned done = __hip_atomic_fetch_add(&a.tickets[n], 1u, __ATOMIC_RELEASE,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (done == (unsigned)a.tiles_per_image - 1u);
+    // The update that completes the image read every other workgroup's
+    // (they form one release sequence): acquire them before the barrier
+    // hands the result to the other threads.
+    if (last_flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   if (!last_flag) return;
