@@ -235,11 +235,15 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   WeightStageB<CI, CO, TAPS, THREADS> wstage;
   wstage.load(a.w, tid);
   float bias[NT];
+  // The GELU epilogue works on halved values (weights, bias and s staged at
+  // half scale, exactly): bit-identical, one multiplication fewer per output.
+  constexpr float kScale = EPI == kReluHswish ? 1.0f : 0.5f;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? a.b[16 * nt + col] : 0.0f;
+  for (int nt = 0; nt < NT; ++nt) bias[nt] = a.b ? kScale * a.b[16 * nt + col] : 0.0f;
   float sadd[NT];  // per-channel term of the GELU epilogue
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) sadd[nt] = EPI == kReluHswish ? 0.0f : a.s[16 * nt + col];
+  for (int nt = 0; nt < NT; ++nt) sadd[nt] = EPI == kReluHswish ? 0.0f : kScale * a.s[16 * nt + col];
+  const float lo_half = kScale * a.lo, hi_half = kScale * a.hi;
   // The first K-step's MFMAs start from the bias (as their C operand), so
   // the accumulators need no initialising copies.
   v4f bias4[NT];
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
   // relative to a strip's first output pixel.
   const int sofs = VSTORE ? (col * a.P + 4 * g) * 4 : 0;
   if (first >= a.items) return;  // workgroup-uniform
-  wstage.place(ws, a.w, tid);
+  wstage.place(ws, a.w, tid, kScale);
   put();
   __syncthreads();  // weights in place; from here on only the per-round barrier
 
@@ -297,15 +301,18 @@ __global__ __launch_bounds__(THREADS, 4) void conv2d_relu_hswish_kernel(Conv2dAr
 
     // The window has been read (the MFMAs above consumed every value), so the
     // next strip's window may overwrite it; this wave's LDS operations run in
-    // program order.
+    // program order.  The scheduling barrier keeps the LDS writes, and their
+    // wait for the window loads, after the MFMAs (with a short K-loop the
+    // scheduler would hoist them above, exposing the loads' latency).
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     put();
 
     auto epilogue = [&](float v, int nt) {
       if constexpr (EPI == kReluHswish)
         return relu_hswish(v);
       else
-        return lrelu_add_clamp_gelu_value<EPI == kGeluSeries>(v, sadd[nt], a.slope, a.lo, a.hi);
+        return lrelu_add_clamp_gelu_half<EPI == kGeluSeries>(v, sadd[nt], a.slope, lo_half, hi_half);
     };
 #pragma unroll
     for (int j = 0; j < MT; ++j)
