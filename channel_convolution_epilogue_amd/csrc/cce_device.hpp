@@ -205,7 +205,8 @@ __device__ __forceinline__ float lrelu_add_clamp_gelu_value(float v, float s, fl
 // the chain, and GELU(c) = 0.5 c (1 + erf(c / sqrt 2)) becomes
 // c' (1 + erf(c' sqrt 2)) with c' = c / 2 (fp32 sqrt 2 is exactly twice fp32
 // 1 / sqrt 2), so the result equals lrelu_add_clamp_gelu_value(v, ...) bit
-// for bit, with one multiplication fewer.
+// for bit (unless some intermediate is subnormal, where halving can drop its
+// last bit), with one multiplication fewer.
 template <bool SERIES>
 __device__ __forceinline__ float lrelu_add_clamp_gelu_half(float h, float s_half, float slope, float lo_half,
                                                            float hi_half) {
