@@ -24,6 +24,13 @@
 //  * Workgroups take row blocks round-robin (remapped so each XCD gets a
 //    contiguous run): neighbouring row blocks of one image run at the same
 //    time and write neighbouring stretches of every output plane.
+//  * A tile's time is set by the busiest SIMD (a barrier ends each tile), so
+//    for the page's layer the row blocks are balanced (62 rows as 7, 8, 8,
+//    8, 7, 8, 8, 8), each workgroup's successive blocks rotate through an
+//    image's row blocks (four rounds give every workgroup 31 rows, where
+//    fixed 8-row blocks gave most of them 32 and one in eight 24), and the
+//    waves take one or two 16-voxel blocks each so that the four SIMDs
+//    share a tile's blocks evenly: 1.482 -> 1.456 ms, bit-identical.
 //  * The epilogue (bias as accumulator init, LeakyReLU, add, clamp, GELU with
 //    erf) runs in registers; only the final value is stored.
 //  * The page's layer (64-float staged rows, 8-row tiles, 16-byte loads)
@@ -162,6 +169,13 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
   // FAST: compile-time row length with 16-byte loads -- buffer-addressed
   // plane staging and (for whole-row tiles) result stores.
   constexpr bool FAST = FIXED_XC != 0 && VLOAD;
+  // BAL (FAST with 16-byte stores, whole-row tiles): balanced row tiles in
+  // a rotating order, and passes of one or two blocks spread so that each
+  // SIMD's four waves share a tile's blocks evenly.  A tile has at most 32
+  // blocks (8 rows of at most XC - KS + 1 voxels, plus 3 + 3 for alignment),
+  // one pass per wave.
+  constexpr bool BAL = FAST && VSTORE;
+  static_assert(!BAL || FIXED_TR * (FIXED_XC - KS + 1) + 6 <= 2 * 16 * WAVES, "one pass per wave");
   static_assert(!FAST || kPrefetchPasses * (THREADS / (FIXED_XC / 4)) >= CI * (FIXED_TR + KS - 1),
                 "a plane fits in the prefetch passes");
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -202,14 +216,32 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
 
   for (int rb = vb; rb < a.nblocks; rb += gridDim.x) {
     const int n = fdiv(rb, a.divRowCol), rc = rb - n * (a.rowtiles * a.coltiles);
-    const int rt = fdiv(rc, a.divCol), ct = rc - rt * a.coltiles;
-    const int h0 = rt * TR, rows = min(TR, a.Ho - h0);
+    int rt = fdiv(rc, a.divCol), h0, rows;
+    const int ct = rc - rt * a.coltiles;
+    if constexpr (BAL) {
+      // Row tiles of floor or ceil(Ho / rowtiles) rows, taken in an order
+      // that rotates with the round (the image's first block index over the
+      // grid), so that the row tiles one workgroup takes in consecutive
+      // rounds are consecutive: 62 rows as 7, 8, 8, 8, 7, 8, 8, 8 give
+      // every workgroup 31 rows over four rounds.
+      rt = (rt + (n * a.rowtiles) / (int)gridDim.x) % a.rowtiles;
+      h0 = (int)((long long)rt * a.Ho / a.rowtiles);
+      rows = (int)((long long)(rt + 1) * a.Ho / a.rowtiles) - h0;
+    } else {
+      h0 = rt * TR;
+      rows = min(TR, a.Ho - h0);
+    }
     const int c0 = ct * a.TC, cols = min(a.TC, a.Wo - c0);
     const bool last_col = ct == a.coltiles - 1;
     const int nr = CI * (rows + KS - 1);                // staged rows per plane
     const int len = min(XC, a.W - c0);                // staged floats per row
     const bool contig = a.coltiles == 1;                // the tile spans whole output rows
-    const int V = rows * cols, MTT = (V + 15) >> 4;     // voxels and 16-voxel blocks
+    // BAL: the tile's voxels are [f_lo, f_hi) of the output plane, taken as
+    // 16-voxel blocks from the 4-aligned s0 up to the 4-aligned e0 (so every
+    // lane's quad is 16-byte aligned); the quads at either end may be partial.
+    const int f_lo = h0 * a.Wo, f_hi = f_lo + rows * a.Wo;
+    const int s0 = BAL ? (f_lo & ~3) : f_lo, e0 = BAL ? ((f_hi + 3) & ~3) : f_hi;
+    const int V = BAL ? e0 - s0 : rows * cols, MTT = (V + 15) >> 4;  // voxels and 16-voxel blocks
     auto src_of = [&](int dd) { return PlaneSrc<CI>{a.x, a.D, a.H, a.W, n, dd, h0, c0}; };
     auto dst_of = [&](int dd) { return PlaneDst<CI>{xs, chstride, (dd % SLOTS) * planestride, XC}; };
     const size_t img = (size_t)CI * a.D * a.H * a.W;  // input floats per image
@@ -256,7 +288,8 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
       // d - 1, which every wave finished before the previous barrier) right
       // after the pass's MFMAs, before any of the tile's result stores, so
       // that waiting for its loads does not also wait for those stores.
-      auto pass = [&](int mb_iv, auto first) {
+      auto pass = [&](int mb_iv, auto first, auto nblk) {
+        constexpr int MT = decltype(nblk)::value;
         // Compiler-only fences: the first keeps the per-step weight reads
         // inside the loop instead of hoisting all 54 of them (216 VGPRs) out
         // of it; the second hides the block index from strength reduction,
@@ -267,7 +300,9 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
         int base[MT][KS];
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
-          const int v = min(16 * (mb + j) + col, V - 1);
+          // Surplus lanes repeat a voxel of the tile (results not stored).
+          const int v = BAL ? min(max(s0 + 16 * (mb + j) + col, f_lo), f_hi - 1) - f_lo
+                            : min(16 * (mb + j) + col, V - 1);
           const int hl = fdiv(v, last_col ? a.divTClast : a.divTC), wl = v - hl * cols;
           const int b0 = g * chstride + hl * XC + wl;
 #pragma unroll
@@ -315,14 +350,18 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
         }
         if constexpr (FAST) {
           if (VSTORE && contig) {
-            // Whole-row tiles: a tile's voxel count and every lane's first
-            // voxel are multiples of 4 (VSTORE), so a lane's quad is whole.
+            // Whole-row tiles: the plane's voxel count and every lane's
+            // first voxel are multiples of 4 (VSTORE), so each lane's quad is
+            // 16-byte aligned; only the tile's first and last quads can be
+            // partial, and store element by element (voxels outside the tile
+            // get an offset past the buffer's end).
             const auto ry = buffer_rsrc(a.y + (size_t)n * CO * vol, (uint32_t)(CO * vol) * 4u);
 #pragma unroll
             for (int j = 0; j < MT; ++j) {
-              const int v0 = 16 * (mb + j) + 4 * g;
-              if (v0 >= V) continue;
-              const uint32_t voff = sofs + (uint32_t)(d * a.Ho * a.Wo + h0 * a.Wo + 16 * (mb + j)) * 4u;
+              const int q0 = s0 + 16 * (mb + j) + 4 * g;  // this lane's first voxel in the plane
+              if (q0 >= e0) continue;
+              const bool whole = q0 >= f_lo && q0 + 4 <= f_hi;
+              const uint32_t voff = sofs + (uint32_t)(d * a.Ho * a.Wo + s0 + 16 * (mb + j)) * 4u;
 #pragma unroll
               for (int nt = 0; nt < NT; ++nt) {
                 const float sadd = ep[CO + 16 * nt + col];
@@ -331,7 +370,14 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
                 r.y = lrelu_add_clamp_gelu_half<SERIES>(r.y, sadd, a.slope, lo_half, hi_half);
                 r.z = lrelu_add_clamp_gelu_half<SERIES>(r.z, sadd, a.slope, lo_half, hi_half);
                 r.w = lrelu_add_clamp_gelu_half<SERIES>(r.w, sadd, a.slope, lo_half, hi_half);
-                buffer_store4(ry, r, voff + (uint32_t)(16 * nt * vol) * 4u);
+                const uint32_t o = voff + (uint32_t)(16 * nt * vol) * 4u;
+                if (whole) {
+                  buffer_store4(ry, r, o);
+                } else {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    buffer_store1(ry, r[e], q0 + e >= f_lo && q0 + e < f_hi ? o + 4u * e : kBufferOOB);
+                }
               }
             }
             return;
@@ -380,17 +426,30 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
         }
       };
 
-      if constexpr (FAST) {
+      using One = std::integral_constant<int, 1>;
+      using Two = std::integral_constant<int, 2>;
+      if constexpr (BAL) {
+        // MTT <= 32 blocks: the first MTT - 16 waves take two blocks, the
+        // rest one (waves w, w + 4, w + 8, w + 12 share a SIMD, so each SIMD
+        // gets a quarter of the blocks, rounded up).
+        const int w = __builtin_amdgcn_readfirstlane(wave), q = max(MTT - WAVES, 0);
+        if (w < q)
+          pass(2 * w, std::true_type(), Two());
+        else if (q + w < MTT)
+          pass(q + w, std::true_type(), One());
+        else
+          fp.store(xs + ((d + KS) % SLOTS) * planestride);  // a wave with no block
+      } else if constexpr (FAST) {
         const int mb0 = MT * __builtin_amdgcn_readfirstlane(wave);
         if (mb0 < MTT)
-          pass(mb0, std::true_type());
+          pass(mb0, std::true_type(), Two());
         else
           fp.store(xs + ((d + KS) % SLOTS) * planestride);  // a wave with no block
 #pragma unroll 1
-        for (int mb_iv = mb0 + MT * WAVES; mb_iv < MTT; mb_iv += MT * WAVES) pass(mb_iv, std::false_type());
+        for (int mb_iv = mb0 + MT * WAVES; mb_iv < MTT; mb_iv += MT * WAVES) pass(mb_iv, std::false_type(), Two());
       } else {
 #pragma unroll 1
-        for (int mb_iv = MT * wave; mb_iv < MTT; mb_iv += MT * WAVES) pass(mb_iv, std::false_type());
+        for (int mb_iv = MT * wave; mb_iv < MTT; mb_iv += MT * WAVES) pass(mb_iv, std::false_type(), Two());
       }
 
       // Plane d + KS goes to slot (d + KS) % (KS + 1), last read by tile d - 1, which
