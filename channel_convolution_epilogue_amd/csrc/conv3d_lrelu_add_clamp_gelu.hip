@@ -83,6 +83,8 @@ struct Conv3dArgs {
   int nblocks;      // N * rowtiles * coltiles row-column blocks
   int chstride;     // floats between channels in LDS (KS + 1 planes + padding)
   int planestride;  // floats between ring slots, (TR + 2) * XC
+  int ych;          // output channels per image in y (CO, or more when a
+                    // launch writes a slice of the channels)
   float slope, lo, hi;
   FastDiv divRowCol, divCol, divTC, divTClast;
 };
@@ -170,12 +172,10 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
   // plane staging and (for whole-row tiles) result stores.
   constexpr bool FAST = FIXED_XC != 0 && VLOAD;
   // BAL (FAST with 16-byte stores, whole-row tiles): balanced row tiles in
-  // a rotating order, and passes of one or two blocks spread so that each
-  // SIMD's four waves share a tile's blocks evenly.  A tile has at most 32
-  // blocks (8 rows of at most XC - KS + 1 voxels, plus 3 + 3 for alignment),
-  // one pass per wave.
+  // a rotating order.  A FAST tile has at most 32 blocks (8 rows of at most
+  // XC - KS + 1 voxels, plus 3 + 3 for alignment): one pass per wave.
   constexpr bool BAL = FAST && VSTORE;
-  static_assert(!BAL || FIXED_TR * (FIXED_XC - KS + 1) + 6 <= 2 * 16 * WAVES, "one pass per wave");
+  static_assert(!FAST || FIXED_TR * (FIXED_XC - KS + 1) + 6 <= MT * 16 * WAVES, "one pass per wave");
   static_assert(!FAST || kPrefetchPasses * (THREADS / (FIXED_XC / 4)) >= CI * (FIXED_TR + KS - 1),
                 "a plane fits in the prefetch passes");
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
       int so[KS];  // ring slot offsets of planes d .. d + KS - 1
 #pragma unroll
       for (int kd = 0; kd < KS; ++kd) so[kd] = ((d + kd) % SLOTS) * planestride;
-      float *ytile = a.y + (size_t)n * CO * vol + (size_t)d * a.Ho * a.Wo;  // uniform
+      float *ytile = a.y + (size_t)n * a.ych * vol + (size_t)d * a.Ho * a.Wo;  // uniform
 
       // One pass: blocks mb_iv, mb_iv + 1 of the tile.  FIRST (FAST only):
       // plane d + KS goes to slot (d + KS) % (KS + 1) (last read by tile
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
             // 16-byte aligned; only the tile's first and last quads can be
             // partial, and store element by element (voxels outside the tile
             // get an offset past the buffer's end).
-            const auto ry = buffer_rsrc(a.y + (size_t)n * CO * vol, (uint32_t)(CO * vol) * 4u);
+            const auto ry = buffer_rsrc(a.y + (size_t)n * a.ych * vol, (uint32_t)(CO * vol) * 4u);
 #pragma unroll
             for (int j = 0; j < MT; ++j) {
               const int q0 = s0 + 16 * (mb + j) + 4 * g;  // this lane's first voxel in the plane
@@ -428,28 +428,25 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
 
       using One = std::integral_constant<int, 1>;
       using Two = std::integral_constant<int, 2>;
-      if constexpr (BAL) {
-        // MTT <= 32 blocks: the first MTT - 16 waves take two blocks, the
+      using First = std::integral_constant<bool, FAST>;
+      if (MTT <= MT * WAVES) {
+        // One pass per wave: the first MTT - 16 waves take two blocks, the
         // rest one (waves w, w + 4, w + 8, w + 12 share a SIMD, so each SIMD
-        // gets a quarter of the blocks, rounded up).
+        // gets a quarter of the blocks, rounded up).  Always the case for
+        // FAST (8 rows of at most 62 voxels, plus alignment).
         const int w = __builtin_amdgcn_readfirstlane(wave), q = max(MTT - WAVES, 0);
-        if (w < q)
-          pass(2 * w, std::true_type(), Two());
-        else if (q + w < MTT)
-          pass(q + w, std::true_type(), One());
-        else
-          fp.store(xs + ((d + KS) % SLOTS) * planestride);  // a wave with no block
-      } else if constexpr (FAST) {
-        const int mb0 = MT * __builtin_amdgcn_readfirstlane(wave);
-        if (mb0 < MTT)
-          pass(mb0, std::true_type(), Two());
-        else
-          fp.store(xs + ((d + KS) % SLOTS) * planestride);  // a wave with no block
-#pragma unroll 1
-        for (int mb_iv = mb0 + MT * WAVES; mb_iv < MTT; mb_iv += MT * WAVES) pass(mb_iv, std::false_type(), Two());
+        if (w < q) {
+          pass(2 * w, First(), Two());
+        } else if (q + w < MTT) {
+          pass(q + w, First(), One());
+        } else {
+          if constexpr (FAST) fp.store(xs + ((d + KS) % SLOTS) * planestride);  // a wave with no block
+        }
       } else {
+        if constexpr (!FAST) {
 #pragma unroll 1
-        for (int mb_iv = MT * wave; mb_iv < MTT; mb_iv += MT * WAVES) pass(mb_iv, std::false_type(), Two());
+          for (int mb_iv = MT * wave; mb_iv < MTT; mb_iv += MT * WAVES) pass(mb_iv, First(), Two());
+        }
       }
 
       // Plane d + KS goes to slot (d + KS) % (KS + 1), last read by tile d - 1, which
@@ -503,10 +500,12 @@ size_t ring_floats(int tr, int xc, int *planestride, int *chstride) {
 // Tiling of one layer shape and its launch: 16-byte loads and stores where
 // sizes and alignment allow, the polynomial GELU when [lo, hi] lies in
 // [-1, 1].  FIXED64: also the instances with compile-time LDS offsets for
-// 64-wide rows in 8-row tiles (the page's layer).
+// 64-wide rows in 8-row tiles (the page's layer).  ych: output channels per
+// image in y (L::CO unless the launch writes a slice of y's channels).
 template <class L, bool FIXED64>
 int launch_layer(const float *x, const float *w, const float *b, const float *s, float *y, int N,
-                 int D, int H, int W, float slope, float lo, float hi, hipStream_t stream) {
+                 int D, int H, int W, float slope, float lo, float hi, hipStream_t stream,
+                 int ych = L::CO) {
   constexpr size_t EXTRA = L::WS_FLOATS + 2 * L::CO;  // weights, bias and s beside the ring
   DeviceInfo dev;
   if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
@@ -516,6 +515,7 @@ int launch_layer(const float *x, const float *w, const float *b, const float *s,
   a.b = b;
   a.s = s;
   a.y = y;
+  a.ych = ych;
   a.D = D;
   a.H = H;
   a.W = W;
@@ -605,8 +605,34 @@ int launch_conv3d_lrelu_add_clamp_gelu(const float *x, const float *w, const flo
     return launch_layer<Layer3<CI, CO, KS>, false>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
   CCE_CONV3D_LAYER(4, 16, 3) CCE_CONV3D_LAYER(4, 32, 3) CCE_CONV3D_LAYER(4, 64, 3)
   CCE_CONV3D_LAYER(8, 16, 3) CCE_CONV3D_LAYER(8, 32, 3)
-  CCE_CONV3D_LAYER(16, 16, 3) CCE_CONV3D_LAYER(16, 32, 3) CCE_CONV3D_LAYER(16, 64, 3)
+  CCE_CONV3D_LAYER(16, 16, 3) CCE_CONV3D_LAYER(16, 32, 3)
 #undef CCE_CONV3D_LAYER
+  // 16 -> 64: its 110 KB weight leaves LDS for whole-row tiles of 4 rows
+  // only up to 34-float rows; wider rows went to column tiles (8 x 12
+  // voxels for W = 64, 6 of a tile's 32 block slots: 0.40 of peak at N = 32,
+  // 16 x 64 x 64).  There, two launches of the 16 -> 32 kernel, each with
+  // half the weight, bias and s, write output channels 0-31 and 32-63 of
+  // every image from 4-row whole-row tiles (0.75 of peak; the input is read
+  // twice, 16 of the 80 channels moved per output voxel).
+  if (C_in == 16 && C_out == 64 && k == 3) {
+    using Full = Layer3<16, 64, 3>;
+    using Half = Layer3<16, 32, 3>;
+    DeviceInfo dev;
+    if (current_device_info(&dev) != CCE_OK) return CCE_ERR_LAUNCH;
+    const bool vl = (W % 4 == 0) && ((uintptr_t)x % 16 == 0);
+    int ps, cs;
+    const size_t need = Full::WS_FLOATS + 2 * Full::CO + ring_floats<Full>(4, vl ? ((W + 3) & ~3) : W, &ps, &cs);
+    if (need * sizeof(float) <= dev.lds_per_block)
+      return launch_layer<Full, false>(x, w, b, s, y, N, D, H, W, slope, lo, hi, stream);
+    const size_t vol = (size_t)(D - 2) * (H - 2) * (W - 2);
+    for (int h = 0; h < 2; ++h) {
+      const int st = launch_layer<Half, false>(x, w + (size_t)h * 32 * 16 * 27, b ? b + 32 * h : nullptr,
+                                               s + 32 * h, y + (size_t)h * 32 * vol, N, D, H, W, slope,
+                                               lo, hi, stream, 64);
+      if (st != CCE_OK) return st;
+    }
+    return CCE_OK;
+  }
   return CCE_ERR_UNSUPPORTED;
 }
 

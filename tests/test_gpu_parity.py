@@ -153,14 +153,33 @@ def test_conv3d_small(cce, N, D, H, W, bias):
 def test_conv3d_other_layer_shapes(cce, C_in, C_out, H, W, lo, hi):
     """Channel counts beyond the page's 8 -> 64 (3 x 3 x 3).  13 x 21 takes the
     scalar loads and stores, 14 x 24 the 16-byte ones; clamp bounds inside
-    [-1, 1] the polynomial GELU, wider ones erff.  16 -> 64 leaves so little
-    LDS beside its weights that its rows are split into column tiles."""
+    [-1, 1] the polynomial GELU, wider ones erff.  16 -> 64 at these widths
+    is one launch with 4-row tiles beside its 110 KB weight (wider rows take
+    two 32-channel launches, tested below)."""
     p = make_inputs(CONV3D, seed=700 + C_in + C_out + W, N=2, C_in=C_in, D=5, H=H, W=W, C_out=C_out, k=3)
     y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, lo, hi)
     torch.cuda.synchronize()
     assert y.shape == (2, C_out, 3, H - 2, W - 2)
     assert_close(y.cpu().numpy(), O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"], 0.2, lo, hi),
                  f"conv3d {C_in}->{C_out} {H}x{W} clamp [{lo}, {hi}]")
+
+
+@pytest.mark.parametrize("N,D,H,W,lo,hi,bias", [
+    (2, 4, 9, 64, -1.0, 1.0, True),    # 16-byte loads and stores, polynomial GELU
+    (1, 5, 12, 50, -2.0, 1.5, True),   # scalar path (W % 4 != 0), erff
+    (3, 3, 7, 40, -1.0, 1.0, False),   # no bias: both halves start from 0
+])
+def test_conv3d_16_to_64_wide_rows(cce, N, D, H, W, lo, hi, bias):
+    """16 -> 64 on rows too wide for whole-row tiles beside the full weight:
+    two launches of the 16 -> 32 kernel, each writing half of every image's
+    output channels with its half of the weight, bias and s."""
+    p = make_inputs(CONV3D, seed=790 + H + W, N=N, C_in=16, D=D, H=H, W=W, C_out=64, k=3)
+    b = dev(p["b"]) if bias else None
+    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), b, dev(p["s"]), 0.2, lo, hi)
+    torch.cuda.synchronize()
+    assert y.shape == (N, 64, D - 2, H - 2, W - 2)
+    ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"] if bias else None, p["s"], 0.2, lo, hi)
+    assert_close(y.cpu().numpy(), ref, f"conv3d 16->64 N={N} {D}x{H}x{W} bias={bias}")
 
 
 @pytest.mark.parametrize("H,W,lo,hi", [(5, 21, -1.0, 1.0), (6, 24, -1.0, 1.0), (6, 24, -2.0, 1.5)])
