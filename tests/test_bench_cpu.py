@@ -95,6 +95,21 @@ def test_record_mfma_counters(tmp_path):
     assert "conv3d_lrelu_add_clamp_gelu_n128" not in bench.record_mfma(tmp_path, prev)
 
 
+def test_committed_counter_records_match_the_kernel_sources():
+    """bench.py reports `traffic` only from a record whose kernel source
+    digest matches the tree: every workload's committed HBM-traffic record,
+    and every convolution's MFMA-counter record, must have been taken on the
+    kernels as they stand."""
+    traffic = json.loads((ROOT / "profiles" / "hbm_traffic.json").read_text())
+    mfma = json.loads((ROOT / "profiles" / "mfma_counters.json").read_text())
+    for name, cfg in WORKLOADS.items():
+        digest = bench.source_digest(cfg["op"])
+        assert traffic[name]["source_sha256_16"] == digest, f"{name}: stale HBM traffic record"
+        assert bench.measured_traffic(cfg["op"], name) == traffic[name]["bytes_per_launch"]
+        if cfg["op"] in ("conv2d_relu_hswish", "conv3d_lrelu_add_clamp_gelu", "convT2d_pool_htanh_mean_tanh"):
+            assert mfma[name]["source_sha256_16"] == digest, f"{name}: stale MFMA counter record"
+
+
 def test_bench_refuses_more_than_one_gpu():
     res = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "8"], capture_output=True,
                          text=True, timeout=120)
