@@ -16,8 +16,8 @@
 //  * Implicit GEMM on the fp32 matrix cores: M = conv-output pixels, N =
 //    C_out output channels (16, 32 or 64: one to four 16-column MFMA
 //    blocks), K = C_in channels x 9 taps (576 for the page's layer).  A tile
-//    is 16 x 32 conv pixels (8 x 16 pooling windows) of one image for 64
-//    output channels (24 x 32 for 32, 32 x 32 for 16); K is walked in
+//    is 16 x 32 conv pixels (8 x 16 pooling windows) of one image for 64 or
+//    32 output channels (32 x 32 for 16); K is walked in
 //    C_in / 8 chunks of 8 input channels whose input halo tile (18 x 34 for
 //    64 channels) and weight slice (8 x 9 x C_out) are staged in LDS.
 //  * The M order puts the four pixels of one 2 x 2 pooling window on four
@@ -64,15 +64,18 @@ static_assert(XOFF + XC <= XRS, "halo row fits the LDS row");
 // Geometry per output-channel count: NT 16-column MFMA blocks; every wave
 // computes MT 16-pixel blocks, RP = MT / 4 row pairs of the tile's 32
 // columns, so a tile has TH = 8 RP rows.  With 64 channels (NT = 4) 8 blocks
-// per wave fill 128 accumulator registers (16 x 32 tiles); with fewer
-// channels a wave takes more blocks -- 12 for 32 channels (24 x 32 tiles), 16
-// for 16 (32 x 32) -- so that each staged chunk and each barrier carry more
-// MFMAs, within the register budget of two waves per SIMD.  The weight slice
-// of one K chunk holds (CC / 4) x 9 x 64 lanes x NT floats.
+// per wave fill 128 accumulator registers (16 x 32 tiles); 16 channels take
+// 16 blocks per wave (32 x 32 tiles), so that each staged chunk and each
+// barrier carry more MFMAs.  32 channels keep 16 x 32 tiles: 16 blocks
+// spill (the 34-row halo chunk's staging registers on top of 128
+// accumulators), and 24 x 32 tiles leave a partial tile row on 2^k-row images
+// and an uneven last round (1408 tiles for 512 workgroup slots at N = 16,
+// 256 x 256): 0.1856 -> 0.1805 ms there, 0.0605 -> 0.0469 ms at 128 x 128.
+// The weight slice of one K chunk holds (CC / 4) x 9 x 64 lanes x NT floats.
 template <int CO_>
 struct OutCh {
   static constexpr int CO = CO_, NT = CO / 16;
-  static constexpr int MT = NT == 4 ? 8 : NT == 2 ? 12 : 16, RP = MT / 4;
+  static constexpr int MT = NT == 1 ? 16 : 8, RP = MT / 4;
   static constexpr int TH = 2 * RP * WAVES, PTH = TH / 2;  // conv-output / pooled rows per tile
   static constexpr int XR = TH + 2;                      // input halo tile rows
   static constexpr int XCS = XR * XRS;  // 16 (mod 64): the lane groups' channels 16 banks apart
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(THREADS, 2) void convT2d_pool_htanh_mean_tanh_kerne
 constexpr size_t kTicketAlign = 256;
 
 // Tiles of a layer: 16 pooling-window columns by OutCh<C_out>::PTH rows (8
-// for 64 output channels, 12 for 32, 16 for 16).
+// for 64 or 32 output channels, 16 for 16).
 void convT_tiles(int H, int W, int C_out, int *tiles_x, int *tiles_per_image) {
   const int PH = H / 2, PW = W / 2;
   const int pth = C_out == 64 ? OutCh<64>::PTH : C_out == 32 ? OutCh<32>::PTH : OutCh<16>::PTH;

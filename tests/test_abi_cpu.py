@@ -150,11 +150,11 @@ def test_convT_workspace_size(lib):
     assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 64, 2, 2, 64) == 256 + wprep + 256
     assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 64, 16, 16, 64, stride=2) == 0
     # other layer shapes: C_in x C_out x 9 prepared weights, C_out partials per tile;
-    # tiles of 16 pooling-window columns by 16 rows (C_out = 16) or 12 rows (C_out = 32)
+    # tiles of 16 pooling-window columns by 16 rows (C_out = 16) or 8 rows (C_out = 32)
     assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(3, 8, 35, 42, 16) == \
         256 + 8 * 16 * 9 * 4 + 3 * (2 * 2) * 16 * 4
     assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(300, 128, 64, 64, 32) == \
-        1280 + 128 * 32 * 9 * 4 + 300 * (3 * 2) * 32 * 4
+        1280 + 128 * 32 * 9 * 4 + 300 * (4 * 2) * 32 * 4
     assert cce.convT2d_pool_htanh_mean_tanh_workspace_bytes(1, 24, 16, 16, 48) == 0
 
 
