@@ -745,8 +745,8 @@ def test_graph_capture_replays_match_eager(cce):
     replayed three times, with eager work and a synchronisation between the
     replays: every replay matches the eager results bit for bit.  The calls
     allocate nothing and issue no memset, so they are capturable; the ConvT
-    workspace is passed in, zeroed before capture, and left zeroed by the
-    kernel."""
+    workspace is passed in, and each call's preparation kernel (captured with
+    it) zeroes the workspace's counters."""
     p2 = make_inputs(CONV2D, seed=801, N=2, C_in=8, H=21, W=30, C_out=64, k=3)
     p3 = make_inputs(CONV3D, seed=802, N=1, C_in=8, D=5, H=12, W=16, C_out=64, k=3)
     pt = make_inputs(CONVT, seed=803, N=2, C_in=64, H=18, W=20, C_out=64, k=3)
