@@ -404,9 +404,12 @@ struct EpiParams {
   float slope = 0.0f, lo = 0.0f, hi = 0.0f;
 };
 
-template <class GEO, int EPI = kReluHswish>
+// GEO serves the 16-byte window loads, GEO_S the scalar ones (a taller
+// strip's scalar window prefetch can spill where its 16-byte one does not).
+template <class GEO, int EPI = kReluHswish, class GEO_S = GEO>
 int launch_layer(const float *x, const float *w, const float *b, float *y, int N, int H, int W,
                  hipStream_t stream, const EpiParams &ep = EpiParams()) {
+  static_assert(GEO::CI == GEO_S::CI && GEO::CO == GEO_S::CO && GEO::KS == GEO_S::KS, "one layer shape");
   Conv2dArgs a;
   a.x = x;
   a.w = w;
@@ -432,17 +435,24 @@ int launch_layer(const float *x, const float *w, const float *b, float *y, int N
       const int sh = (r * (a.Wo & 3)) & 3;
       if (sh > sh_max) sh_max = sh;
     }
-  a.S = (a.Wo + sh_max + GEO::SW - 1) / GEO::SW;
-  a.G = (a.Ho + GEO::RB - 1) / GEO::RB;
-  const long long items = (long long)N * a.G * a.S;
-  if (items >= (1LL << 31) - (1LL << 24)) return CCE_ERR_TOO_LARGE;
-  a.items = (int)items;
-  a.divS = make_fastdiv((uint32_t)a.S);
-  a.divG = make_fastdiv((uint32_t)a.G);
+  auto strips = [&](int sw, int rb) {
+    a.S = (a.Wo + sh_max + sw - 1) / sw;
+    a.G = (a.Ho + rb - 1) / rb;
+    const long long items = (long long)N * a.G * a.S;
+    if (items >= (1LL << 31) - (1LL << 24)) return false;
+    a.items = (int)items;
+    a.divS = make_fastdiv((uint32_t)a.S);
+    a.divG = make_fastdiv((uint32_t)a.G);
+    return true;
+  };
 
-  if (vl)
+  if (vl) {
+    if (!strips(GEO::SW, GEO::RB)) return CCE_ERR_TOO_LARGE;
     return vs ? launch_instance<GEO, true, true, EPI>(a, stream) : launch_instance<GEO, true, false, EPI>(a, stream);
-  return vs ? launch_instance<GEO, false, true, EPI>(a, stream) : launch_instance<GEO, false, false, EPI>(a, stream);
+  }
+  if (!strips(GEO_S::SW, GEO_S::RB)) return CCE_ERR_TOO_LARGE;
+  return vs ? launch_instance<GEO_S, false, true, EPI>(a, stream)
+            : launch_instance<GEO_S, false, false, EPI>(a, stream);
 }
 
 }  // namespace
@@ -462,9 +472,16 @@ int launch_conv2d_relu_hswish(const float *x, const float *w, const float *b, fl
   // up to 8 input channels).  The 16-byte paths matter as much here: with
   // scalar loads the 16-channel and 5 x 5 windows (15-18 floats per lane in
   // flight) spill, and 16 -> 64, 3 x 3 ran at 0.31 instead of 0.69 of peak.
+  // With 16 or 32 output channels a 1 x 16 strip carries only 1 or 2 MFMAs
+  // per K-step against the same window staging, addressing and barrier:
+  // their 16-byte instances take 2 x 16 strips (N = 32, 128 x 128: 8 -> 16,
+  // 3 x 3 0.0176 -> 0.0167 ms, 16 -> 32 0.0482 -> 0.0463, 8 -> 16, 5 x 5
+  // 0.0382 -> 0.0345, 4 -> 16, 1 x 1 0.0100 -> 0.0092).  With 64 channels
+  // 2 x 16 strips gained nothing; their scalar instances spill.
 #define CCE_CONV2D_LAYER(CI, CO, KS)                                                        \
   if (C_in == CI && C_out == CO && k == KS)                                                \
-    return launch_layer<StripGeo<1, 1, CI, CO, KS>>(x, w, b, y, N, H, W, stream);
+    return launch_layer<StripGeo<CO <= 32 ? 2 : 1, 1, CI, CO, KS>, kReluHswish,              \
+                        StripGeo<1, 1, CI, CO, KS>>(x, w, b, y, N, H, W, stream);
 #define CCE_CONV2D_LAYERS_CO(CI, KS) \
   CCE_CONV2D_LAYER(CI, 16, KS) CCE_CONV2D_LAYER(CI, 32, KS) CCE_CONV2D_LAYER(CI, 64, KS)
   CCE_CONV2D_LAYERS_CO(4, 1) CCE_CONV2D_LAYERS_CO(8, 1) CCE_CONV2D_LAYERS_CO(16, 1)

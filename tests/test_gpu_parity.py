@@ -84,14 +84,16 @@ def test_conv2d_small(cce, N, H, W, bias):
     assert_close(y.cpu().numpy(), O.conv2d_relu_hswish(p["x"], p["w"], b), f"conv2d N={N} {H}x{W}")
 
 
-@pytest.mark.parametrize("H,W", [(19, 23), (20, 24)])
+@pytest.mark.parametrize("H,W", [(19, 23), (20, 24), (21, 24)])
 @pytest.mark.parametrize("C_in,C_out,k", [(4, 16, 1), (8, 32, 3), (16, 64, 3), (4, 64, 5), (8, 16, 5),
                                          (16, 32, 1), (8, 64, 1), (4, 32, 3)])
 def test_conv2d_other_layer_shapes(cce, C_in, C_out, k, H, W):
     """Layer shapes beyond the page's 8 -> 64, 3 x 3 (other channel counts and
     kernel sizes): 19 x 23 takes the scalar loads and stores and leaves ragged
-    strips and row groups; 20 x 24 (W and the output plane multiples of 4)
-    the 16-byte ones."""
+    strips and row groups; 20 x 24 and 21 x 24 (W and the output plane
+    multiples of 4) the 16-byte ones, which for 16 or 32 output channels run
+    2-row strips (21 x 24: an odd output height, so the last row pair has
+    one row)."""
     p = make_inputs(CONV2D, seed=600 + C_in + C_out + k + W, N=2, C_in=C_in, H=H, W=W, C_out=C_out, k=k)
     y = cce.conv2d_relu_hswish(dev(p["x"]), dev(p["w"]), dev(p["b"]))
     torch.cuda.synchronize()
