@@ -2,9 +2,9 @@
  * cce.h -- C ABI of the fused small-channel convolution + epilogue library
  * (libcce.so, HIP kernels for AMD MI355X / gfx950).
  *
- * Three fused operators, each one kernel launch that reads its input and
- * weights from device memory and writes only its final output (the
- * convolution result never reaches device memory):
+ * Three fused operators whose kernels read the input and weights from
+ * device memory and write only the final output (the convolution result
+ * never reaches device memory):
  *
  *   conv2d_relu_hswish            Conv2d k x k (stride 1, padding 0) -> ReLU -> HardSwish
  *   conv3d_lrelu_add_clamp_gelu   Conv3d k^3 (stride 1, padding 0) -> LeakyReLU -> + s[c]
@@ -115,7 +115,9 @@ int conv2d_relu_hswish(const float *x, const float *w, const float *b, float *y,
  * page's 3 x 3 x 3, 8 -> 64 included); 16-byte loads and stores where sizes
  * and alignment allow; a fitted polynomial for GELU when [lo, hi] lies in
  * [-1, 1], erff otherwise; any N >= 1, D, H, W >= k (rows too wide for LDS are split into
- * column tiles); lo <= hi and all three scalars finite;
+ * column tiles; a 3 x 3 x 3, 16 -> 64 layer with rows wider than 34 floats runs
+ * as two launches, each writing 32 of the output channels); lo <= hi and all
+ * three scalars finite;
  * N*C_out*(D-k+1)*(H-k+1)*(W-k+1) < 2^31.  Anything else returns
  * CCE_ERR_UNSUPPORTED (or CCE_ERR_SHAPE / CCE_ERR_TOO_LARGE).
  */
