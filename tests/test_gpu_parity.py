@@ -222,23 +222,24 @@ def test_conv3d_page_layer_instance_edges(cce, N, D, H, W, lo, hi):
     assert_close(y.cpu().numpy(), ref, f"conv3d N={N} {D}x{H}x{W} clamp [{lo}, {hi}]")
 
 
-@pytest.mark.parametrize("N,D,H", [
-    (4, 9, 16),    # 14 rows as 7 + 7: the second block starts mid-quad (7 x 62 = 434)
-    (2, 4, 12),    # 10 rows as 5 + 5
-    (3, 5, 4),     # one 2-row block per image
-    (2, 4, 128),   # 126 rows in 16 blocks of 7 and 8
-    (5, 6, 30),    # 28 rows as 7, 7, 7, 7
-    (40, 3, 64),   # 320 row blocks: more than one round, so the rotation is not 0
+@pytest.mark.parametrize("N,D,H,lo,hi", [
+    (4, 9, 16, -1.0, 1.0),    # 14 rows as 7 + 7: the second block starts mid-quad (7 x 62 = 434)
+    (4, 9, 16, -2.0, 1.5),    # the same with erff (clamp bounds outside [-1, 1])
+    (2, 4, 12, -1.0, 1.0),    # 10 rows as 5 + 5
+    (3, 5, 4, -1.0, 1.0),     # one 2-row block per image
+    (2, 4, 128, -1.0, 1.0),   # 126 rows in 16 blocks of 7 and 8
+    (5, 6, 30, -1.0, 1.0),    # 28 rows as 7, 7, 7, 7
+    (40, 3, 64, -1.0, 1.0),   # 320 row blocks: more than one round, so the rotation is not 0
 ])
-def test_conv3d_balanced_row_tiles(cce, N, D, H):
+def test_conv3d_balanced_row_tiles(cce, N, D, H, lo, hi):
     """The page's layer (64-wide rows) with an even number of output rows:
     balanced row blocks whose first voxel need not be quad-aligned (partial
     first and last quads), one- and two-block passes, rotated block order."""
     p = make_inputs(CONV3D, seed=280 + N + D + H, N=N, C_in=8, D=D, H=H, W=64, C_out=64, k=3)
-    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, -1.0, 1.0)
+    y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, lo, hi)
     torch.cuda.synchronize()
-    ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"], 0.2, -1.0, 1.0)
-    assert_close(y.cpu().numpy(), ref, f"conv3d N={N} {D}x{H}x64")
+    ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"], 0.2, lo, hi)
+    assert_close(y.cpu().numpy(), ref, f"conv3d N={N} {D}x{H}x64 clamp [{lo}, {hi}]")
 
 
 def test_conv3d_workload_n128_full(cce):
