@@ -19,8 +19,8 @@
 //  * The 216 x 64 weight sits in LDS in B-operand order (55 KB): one 16-byte
 //    read per K-step gives a lane its B values for all four 16-channel blocks,
 //    so each A value read from LDS feeds four MFMAs.  Every wave of the
-//    16-wave workgroup computes two 16-voxel blocks x 64 channels per tile:
-//    eight independent accumulator chains.
+//    16-wave workgroup computes one or two 16-voxel blocks x 64 channels per
+//    tile pass: four or eight independent accumulator chains.
 //  * Workgroups take row blocks round-robin (remapped so each XCD gets a
 //    contiguous run): neighbouring row blocks of one image run at the same
 //    time and write neighbouring stretches of every output plane.
@@ -65,7 +65,7 @@ struct Layer3 {
   static constexpr int WS_FLOATS = KSTEPS * 64 * NT;  // weights, B-operand order (55 KB for 8 -> 64)
   static_assert(CI % 4 == 0 && CO % 16 == 0 && NT >= 1 && NT <= 4, "layer shape");
 };
-constexpr int MT = 2;                        // 16-voxel blocks per wave per pass
+constexpr int MT = 2;                        // 16-voxel blocks per wave per pass, at most
 constexpr int kPrefetchPasses = 2;           // a plane of 8 x 10 rows of 64 floats takes 2 passes
 
 struct Conv3dArgs {
@@ -283,13 +283,14 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
       for (int kd = 0; kd < KS; ++kd) so[kd] = ((d + kd) % SLOTS) * planestride;
       float *ytile = a.y + (size_t)n * a.ych * vol + (size_t)d * a.Ho * a.Wo;  // uniform
 
-      // One pass: blocks mb_iv, mb_iv + 1 of the tile.  FIRST (FAST only):
-      // plane d + KS goes to slot (d + KS) % (KS + 1) (last read by tile
-      // d - 1, which every wave finished before the previous barrier) right
-      // after the pass's MFMAs, before any of the tile's result stores, so
-      // that waiting for its loads does not also wait for those stores.
+      // One pass: blocks mb_iv .. mb_iv + NB - 1 of the tile (NB = 1 or 2).
+      // FIRST (FAST only): plane d + KS goes to slot (d + KS) % (KS + 1)
+      // (last read by tile d - 1, which every wave finished before the
+      // previous barrier) right after the pass's MFMAs, before any of the
+      // tile's result stores, so that waiting for its loads does not also
+      // wait for those stores.
       auto pass = [&](int mb_iv, auto first, auto nblk) {
-        constexpr int MT = decltype(nblk)::value;
+        constexpr int NB = decltype(nblk)::value;
         // Compiler-only fences: the first keeps the per-step weight reads
         // inside the loop instead of hoisting all 54 of them (216 VGPRs) out
         // of it; the second hides the block index from strength reduction,
@@ -297,9 +298,9 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
         asm volatile("" ::: "memory");
         int mb = mb_iv;
         asm volatile("" : "+v"(mb));
-        int base[MT][KS];
+        int base[NB][KS];
 #pragma unroll
-        for (int j = 0; j < MT; ++j) {
+        for (int j = 0; j < NB; ++j) {
           // Surplus lanes repeat a voxel of the tile (results not stored).
           const int v = BAL ? min(max(s0 + 16 * (mb + j) + col, f_lo), f_hi - 1) - f_lo
                             : min(16 * (mb + j) + col, V - 1);
@@ -308,12 +309,12 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
 #pragma unroll
           for (int kd = 0; kd < KS; ++kd) base[j][kd] = b0 + so[kd];
         }
-        v4f acc[MT][NT];
+        v4f acc[NB][NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const float bias = ep[16 * nt + col];
 #pragma unroll
-          for (int j = 0; j < MT; ++j) acc[j][nt] = splat4(bias);
+          for (int j = 0; j < NB; ++j) acc[j][nt] = splat4(bias);
         }
 
         // The A and B operands of K-step s + 1 are read from LDS while step s's
@@ -322,13 +323,13 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
         // order, so each pass ends with one wave issuing alone; reading its
         // operands a step ahead keeps it from waiting on LDS at every step
         // (1.543 instead of 1.592 ms for the page's workload).
-        float bq[2][NT], aq[2][MT];
+        float bq[2][NT], aq[2][NB];
         auto fetch = [&](int s, int slot) {
           const int tt = s % TAPS, kd = tt / (KS * KS), kh = (tt / KS) % KS, kw = tt % KS;
           const int off = (s / TAPS) * 4 * chstride + kh * XC + kw;
           load_b<NT>(bq[slot], &ws[(s * 64 + lane) * NT]);
 #pragma unroll
-          for (int j = 0; j < MT; ++j) aq[slot][j] = xs[base[j][kd] + off];
+          for (int j = 0; j < NB; ++j) aq[slot][j] = xs[base[j][kd] + off];
         };
         fetch(0, 0);
 #pragma unroll
@@ -336,7 +337,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
           if (s + 1 < KSTEPS) fetch(s + 1, (s + 1) & 1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int j = 0; j < MT; ++j)
+          for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
               acc[j][nt] = mfma16x16x4(aq[s & 1][j], bq[s & 1][nt], acc[j][nt]);
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
             // get an offset past the buffer's end).
             const auto ry = buffer_rsrc(a.y + (size_t)n * a.ych * vol, (uint32_t)(CO * vol) * 4u);
 #pragma unroll
-            for (int j = 0; j < MT; ++j) {
+            for (int j = 0; j < NB; ++j) {
               const int q0 = s0 + 16 * (mb + j) + 4 * g;  // this lane's first voxel in the plane
               if (q0 >= e0) continue;
               const bool whole = q0 >= f_lo && q0 + 4 <= f_hi;
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(THREADS, 4) void conv3d_lrelu_add_clamp_gelu_kernel
           }
         }
 #pragma unroll
-        for (int j = 0; j < MT; ++j) {
+        for (int j = 0; j < NB; ++j) {
           const int v0 = 16 * (mb + j) + 4 * g;  // this lane's first voxel in the tile
           if (v0 >= V) continue;  // (inside the block loop)
           // Output offset of voxel v0 within the (n, channel, d) plane.
