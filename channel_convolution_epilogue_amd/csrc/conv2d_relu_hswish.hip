@@ -9,7 +9,7 @@
 //    peak; the contraction is dense enough (72 x 64 per pixel) to feed them.
 //  * The unit of work is one wave's strip: 16 output columns of one output
 //    row of one image, all 64 channels (one 16-pixel MFMA block per channel
-//    block).  Each wave stages its strip's input window (8 channels x 3 rows
+//    block); layers with 16 or 32 output channels take two rows per strip.  Each wave stages its strip's input window (8 channels x 3 rows
 //    x 24 columns) in a slice of LDS of its own, so no wave ever waits for
 //    another's data.  The next strip's window is loaded into registers while
 //    the current strip's MFMAs run, and written to the wave's slice after
