@@ -857,6 +857,25 @@ def test_random_shape_sweep_conv3d(cce):
         assert_close(y.cpu().numpy(), ref, f"sweep conv3d {c}")
 
 
+def test_random_shape_sweep_conv3d_wide_rows(cce):
+    """Rows of 36-68 floats: the page's layer on 64-wide rows (balanced row
+    blocks), 16 -> 64 as two 32-channel launches, whole-row tiles of fewer
+    rows, even and odd output heights."""
+    def draw(rng):
+        lo, hi = [(-1.0, 1.0), (-2.0, 1.5)][int(rng.integers(0, 2))]
+        return dict(N=int(rng.integers(1, 3)), C_in=int(rng.choice([4, 8, 16])), C_out=int(rng.choice([16, 32, 64])),
+                    D=int(rng.integers(3, 6)), H=int(rng.integers(3, 21)), W=int(rng.choice([36, 40, 50, 64, 64, 68])),
+                    lo=lo, hi=hi)
+    for i, c in enumerate(_sweep_cases(2027, 14, draw)):
+        print(f"sweep conv3d wide case {i}: {c}", flush=True)
+        p = make_inputs(CONV3D, seed=3300 + i, N=c["N"], C_in=c["C_in"], D=c["D"], H=c["H"], W=c["W"],
+                        C_out=c["C_out"], k=3)
+        y = cce.conv3d_lrelu_add_clamp_gelu(dev(p["x"]), dev(p["w"]), dev(p["b"]), dev(p["s"]), 0.2, c["lo"], c["hi"])
+        torch.cuda.synchronize()
+        ref = O.conv3d_lrelu_add_clamp_gelu(p["x"], p["w"], p["b"], p["s"], 0.2, c["lo"], c["hi"])
+        assert_close(y.cpu().numpy(), ref, f"sweep conv3d wide {c}")
+
+
 def test_random_shape_sweep_convT(cce):
     def draw(rng):
         return dict(N=int(rng.integers(1, 3)), C_in=int(8 * rng.integers(1, 9)), C_out=int(rng.choice([16, 32, 64])),
