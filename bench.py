@@ -102,7 +102,11 @@ def measured_traffic(op: str, workload: str):
         rec = json.loads(f.read_text()).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha256_16") != source_digest(op):
+    if not rec:
+        return None
+    if rec.get("source_sha256_16") != source_digest(op):
+        print(f"# {workload}: the HBM-traffic record was taken on another version of "
+              f"{KERNEL_SOURCES[op]}; traffic reported as null", file=sys.stderr)
         return None
     return rec.get("bytes_per_launch")
 
