@@ -1,5 +1,6 @@
 // extern "C" entry points of libcce: argument validation (host only, before any
-// HIP call), then one kernel launch per call.  No allocation, no
+// HIP call), then the call's kernel launches (one, or two for the transposed
+// convolution and the wide-row 16 -> 64 Conv3d).  No allocation, no
 // synchronisation (unless CCE_DEBUG is set) and no mutable global state beyond
 // per-device caches of device properties and of each kernel instance's launch
 // set-up.
